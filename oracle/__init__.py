@@ -1,0 +1,7 @@
+"""CPU oracle for fused linear cross-entropy (test infrastructure only).
+
+Only the tests, the package's smoke check and the benchmark's CPU-baseline
+leg may import this package; the product path never does.
+"""
+from .flce_oracle import *  # noqa: F401,F403
+from .flce_oracle import Forward, Problem  # noqa: F401
