@@ -1,0 +1,198 @@
+#!/usr/bin/env python3
+"""Fused linear cross-entropy forward + backward throughput on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload 2]
+
+One step is flce_forward followed by flce_backward (every kernel of the hot
+path) over one batch of synthetic inputs already resident in HBM.  Prints
+one JSON line: tokens/s, the % of the bf16 dense MFMA peak that the credited
+work (8 Tv Vu H flops: projection, recompute, dX and dW) reaches, a roofline
+entry for the dominant kernel from HIP events recorded around each of its
+launches inside the timed region, and the CPU oracle timed on a bounded slice
+of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 flop/clk/CU, dense bf16 MFMA
+METRIC = "fused linear-CE fwd+bwd tokens/sec on 1 MI355X; % of bf16 MFMA peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(inp, n_tokens):
+    """Time the oracle (fwd + bwd, full vocabulary) on the first n_tokens
+    positions of the workload; returns tokens/s and what was run."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"),
+                      default=os.cpu_count())
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    X = oracle.to_f64(inp["hidden"][:n_tokens].cpu())
+    W = oracle.head_values(inp["weight"].cpu())
+    y = inp["labels"][:n_tokens].cpu().numpy()
+    p = oracle.Problem(inp["unpadded_vocab"], inp["softcap"], inp["ignore_index"], inp["reduction"],
+                       inp["num_label_tokens"])
+    t0 = time.perf_counter()
+    oracle.forward(X, W, y, p, row_block=256)
+    oracle.backward(X, W, y, p, row_block=256)
+    dt = time.perf_counter() - t0
+    return {
+        "value": n_tokens / dt,
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"first {n_tokens} positions of the workload, fwd+bwd over the full vocabulary "
+                  f"(fp64 numpy, {dt:.1f} s)",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM bytes per launch of the dominant kernel, from rocprofv3 counters")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the fused linear cross-entropy path is built and timed on a "
+              "single MI355X; runs on more than one GPU are not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import lm_head_cross_amd as L
+    from workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    log(f"workload {w.key}: {w.name}")
+    inp = make_inputs(w, device="cuda:0", argmax_device="cuda:0")
+    X, y = inp["hidden"], inp["labels"]
+    W = inp["weight"]
+    if W.dtype == torch.float32:
+        W = L.flce_round_to_bf16(W)
+    T, H, V, Vu = w.T, w.H, w.V, w.Vu
+    Tv = inp["n_valid"]
+    p = L.make_problem(T, H, V, Vu, w.softcap, inp["ignore_index"], w.reduction, inp["num_label_tokens"])
+    ws = L.alloc_workspace(p, dev)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    lse = torch.empty(T, dtype=torch.float32, device=dev)
+    g = torch.ones((), dtype=torch.float32, device=dev)
+    dX = torch.empty_like(X)
+    dW = torch.empty((V, H), dtype=torch.float32, device=dev)
+
+    def step():
+        L.flce_forward(p, X, W, y, loss, lse, workspace=ws)
+        L.flce_backward(p, X, W, y, lse, g, dX, dW, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    trace = L.LaunchTrace(capacity=max(64, 64 * args.steps)).start()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    trace.stop()
+    ms = e0.elapsed_time(e1) / args.steps
+    records = trace.records()
+
+    kinds = {}
+    for kind, kms, fl in records:
+        k = kinds.setdefault(kind, {"launches": 0, "ms": 0.0, "flops": 0.0})
+        k["launches"] += 1
+        k["ms"] += kms
+        k["flops"] += fl
+    for name, k in sorted(kinds.items(), key=lambda kv: -kv[1]["ms"]):
+        tf = k["flops"] / (k["ms"] * 1e-3) / 1e12 if k["flops"] else 0.0
+        log(f"  {name:12s} launches={k['launches']:5d} total={k['ms'] / args.steps:8.3f} ms/step "
+            f"avg={k['ms'] / k['launches'] * 1e3:9.1f} us" + (f"  {tf:7.1f} TFLOP/s (algorithmic)" if tf else ""))
+    dom_name, dom = max(kinds.items(), key=lambda kv: kv[1]["ms"])
+    achieved = dom["flops"] / (dom["ms"] * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        with open(args.traffic_json) as f:
+            tj = json.load(f)
+        entry = tj.get(f"workload{w.key}", {}).get(dom_name)
+        if entry and entry.get("source_hash") == tj.get("kernel_source_hash"):
+            traffic = entry.get("bytes_per_launch")
+    roofline = {
+        "kernel": dom_name,
+        "bound": "mfma",
+        "achieved": round(achieved, 1),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": traffic,
+        "avg_launch_us": round(dom["ms"] / dom["launches"] * 1e3, 1),
+        "flops_per_launch": dom["flops"] / dom["launches"],
+    }
+    credited = 8.0 * Tv * Vu * H
+    tokens_per_s = T / (ms * 1e-3)
+    pct_peak = credited / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12) * 100.0
+    log(f"step {ms:.3f} ms  {tokens_per_s:,.0f} tokens/s  {pct_peak:.1f}% of bf16 peak "
+        f"(credited {credited / 1e12:.2f} TFLOP)  loss={loss.item():.6g}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle on {args.cpu_tokens} tokens ...")
+        cpu = cpu_baseline(inp, args.cpu_tokens)
+        log(f"  oracle {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_of_bf16_peak": round(pct_peak, 2),
+        "config": {
+            "workload": w.name,
+            "tokens": T, "hidden": H, "vocab": V, "unpadded_vocab": Vu, "valid_tokens": Tv,
+            "softcap": w.softcap, "reduction": w.reduction,
+            "num_label_tokens": inp["num_label_tokens"],
+            "credited_tflop_per_step": round(credited / 1e12, 3),
+            "label_tokens_per_s": round(Tv / (ms * 1e-3), 1),
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

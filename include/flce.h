@@ -1,0 +1,223 @@
+/*
+ * flce.h -- C ABI of the fused linear cross-entropy library for AMD MI355X
+ * (gfx950).
+ *
+ * One call computes, for bf16 hidden states X[T,H] and a bf16 head W[V,H]:
+ *
+ *   z[t,v]  = sum_h X[t,h] W[v,h]            fp32 accumulation, v < Vu only
+ *   z'      = c * tanh(z / c)                 if c > 0 (softcap), else z
+ *   lse[t]  = log sum_{v<Vu} exp z'[t,v]
+ *   l[t]    = lse[t] - z'[t, y_t]             0 where y_t == ignore_index
+ *   loss    = (sum_t l[t]) / D
+ *
+ * and the backward pass gives dX = G W[:Vu] and dW[:Vu] = G^T X with
+ * G[t,v] = (g/D) (softmax(z')[t,v] - [v == y_t]) (1 - (z'/c)^2), where g is the
+ * upstream scalar gradient.  The [T,V] logits are never stored: the forward
+ * keeps per-token log-sum-exp partials and the backward recomputes logit tiles
+ * over bounded vocabulary chunks.
+ *
+ * Sources (NVIDIA NeMo AutoModel API pages):
+ *  - "nemo_automodel.components.models.inkling2.loss",
+ *    Inkling2FusedLinearCrossEntropy (constructor and class description):
+ *    bf16 x bf16 projection with fp32 accumulation, softcap and cross entropy
+ *    in fp32, rows at or past unpadded_vocab_size never enter the softmax, an
+ *    fp32 head is rounded to bf16.
+ *  - "nemo_automodel.components.loss.linear_ce", FusedLinearCrossEntropy
+ *    (constructor: ignore_index, logit_softcapping, reduction; forward:
+ *    hidden_states, labels, lm_weight, num_label_tokens; scalar result).
+ *  - "nemo_automodel.components.loss.chunked_ce", _ChunkedCrossEntropySum
+ *    (forward: ignored positions give zero loss and gradient, fp32 scalar
+ *    result, inputs not mutated; backward: fp32 softmax chunks recomputed,
+ *    scalar upstream gradient).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers on the current HIP device,
+ *    row-major and contiguous.  The caller owns every buffer; the library
+ *    allocates no device memory and keeps no state between calls.  Inputs
+ *    are read only.
+ *  - Work is enqueued on `stream` and the call returns without waiting for
+ *    it (no host synchronisation).
+ *  - The return value is an flce_status_t.  Argument errors are detected on
+ *    the host before any device work is enqueued, so a non-zero return means
+ *    nothing was launched (except FLCE_ERR_HIP, which reports a failed launch).
+ *  - A label that is neither ignore_index nor in [0, unpadded_vocab) can only
+ *    be seen on the device: that position is treated as ignored and
+ *    FLCE_DEVICE_BAD_LABEL is OR-ed into *device_status (if not NULL).
+ */
+#ifndef FLCE_H
+#define FLCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum flce_status {
+  FLCE_OK = 0,
+  FLCE_ERR_INVALID_ARG = 1, /* a size, knob or pointer is out of its domain   */
+  FLCE_ERR_UNSUPPORTED = 2, /* valid, but outside what the kernels handle     */
+  FLCE_ERR_WORKSPACE = 3,   /* workspace NULL, misaligned or too small         */
+  FLCE_ERR_HIP = 4          /* a HIP launch failed                             */
+} flce_status_t;
+
+/* Bits OR-ed into the optional device status word. */
+#define FLCE_DEVICE_BAD_LABEL 1
+
+typedef enum flce_reduction {
+  FLCE_REDUCTION_SUM = 0,  /* loss = sum of per-token losses                 */
+  FLCE_REDUCTION_MEAN = 1  /* loss = sum / (number of non-ignored positions) */
+} flce_reduction_t;
+
+typedef enum flce_dtype {
+  FLCE_DTYPE_BF16 = 0
+} flce_dtype_t;
+
+/*
+ * Problem description, shared by every entry point.
+ *
+ * num_tokens        T >= 0: flattened [batch, sequence] positions.
+ * hidden            H > 0, a multiple of 64.
+ * vocab             V: rows of the head, padding included.
+ * unpadded_vocab    Vu, 0 < Vu <= V: rows that take part in the softmax
+ *                   (Inkling2 page, constructor argument unpadded_vocab_size).
+ * softcap           c >= 0 and finite; 0 turns the softcap off (linear_ce page,
+ *                   constructor argument logit_softcapping).
+ * ignore_index      label value of positions that do not count (default -100).
+ * reduction         FLCE_REDUCTION_SUM or FLCE_REDUCTION_MEAN.
+ * num_label_tokens  > 0: divide the summed loss by this count whatever the
+ *                   reduction (linear_ce page, forward argument
+ *                   num_label_tokens); < 0: not given.  0 is invalid.
+ * weight_dtype      FLCE_DTYPE_BF16 (the only head dtype accepted; an fp32
+ *                   head is rounded to bf16 by the caller).
+ */
+typedef struct flce_problem {
+  int64_t num_tokens;
+  int64_t hidden;
+  int64_t vocab;
+  int64_t unpadded_vocab;
+  float softcap;
+  int32_t reduction;
+  int64_t ignore_index;
+  int64_t num_label_tokens;
+  int32_t weight_dtype;
+} flce_problem_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* flce_status_string(int status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int flce_version(void);
+
+/*
+ * Bytes of device workspace the forward and backward calls need for this
+ * problem (one size serves both).  Writes it to *bytes.  The bound keeps every
+ * logit-shaped scratch buffer at most a quarter of a bf16 [T, Vu] array.
+ * Errors: FLCE_ERR_INVALID_ARG / FLCE_ERR_UNSUPPORTED as for flce_forward.
+ */
+int flce_workspace_size(const flce_problem_t* problem, size_t* bytes);
+
+/*
+ * Forward pass.
+ *
+ * hidden       bf16 [T, H], 16-byte aligned.
+ * weight       bf16 [V, H], 16-byte aligned; rows >= Vu are never read.
+ * labels       int64 [T].
+ * loss         fp32 scalar (device): the reduced loss; NaN for MEAN with no
+ *              valid position and no num_label_tokens (0/0, as PyTorch).
+ * lse          fp32 [T] (required): per-token log-sum-exp over the usable
+ *              rows, 0 at ignored positions.  The backward pass reads it.
+ * token_loss   fp32 [T] or NULL: per-token loss, 0 at ignored positions.
+ * device_status int32 scalar or NULL; see FLCE_DEVICE_BAD_LABEL.  It is only
+ *              OR-ed into, never cleared.
+ * workspace    device buffer of at least flce_workspace_size() bytes,
+ *              256-byte aligned; its contents need not be initialised and
+ *              are scratch only after the call.
+ */
+int flce_forward(const flce_problem_t* problem, const void* hidden, const void* weight,
+                 const int64_t* labels, float* loss, float* lse, float* token_loss,
+                 int32_t* device_status, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream);
+
+/*
+ * Backward pass: gradients of grad_out * loss.
+ *
+ * hidden, weight, labels   as passed to flce_forward.
+ * lse          fp32 [T] written by flce_forward for the same inputs.
+ * grad_out     fp32 scalar (device): upstream gradient of the loss.
+ * d_hidden     bf16 [T, H] (output, overwritten): rows of ignored positions 0.
+ * d_weight     fp32 [V, H] (output, overwritten): rows >= Vu are 0.
+ * device_status, workspace  as for flce_forward.
+ *
+ * Results are deterministic: no atomics take part in any sum.
+ */
+int flce_backward(const flce_problem_t* problem, const void* hidden, const void* weight,
+                  const int64_t* labels, const float* lse, const float* grad_out,
+                  void* d_hidden, float* d_weight, int32_t* device_status, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Round an fp32 head to the bf16 compute copy the kernels read: nearest
+ * value, ties to even, NaN stays NaN ("nemo_automodel.components.models.
+ * inkling2.loss", class description: an FP32 head is rounded to BF16, the
+ * cast FSDP applies).
+ *
+ * src    fp32 [count], 4-byte aligned (device).
+ * dst    bf16 [count], 2-byte aligned (device); may not overlap src.
+ * count  >= 0 elements.
+ * Errors: FLCE_ERR_INVALID_ARG for a negative count or a NULL pointer with
+ * count > 0; FLCE_ERR_UNSUPPORTED for misaligned pointers.
+ */
+int flce_round_to_bf16(const float* src, void* dst, int64_t count, hipStream_t stream);
+
+/*
+ * Launch tracing, for measurement.  While a trace is running, every kernel
+ * launch the library makes is bracketed by a pair of HIP events recorded on
+ * the launch's stream, tagged with the kernel's kind below; a caller can then
+ * read each launch's duration.  The trace is process-wide state: start, run
+ * the calls to measure, stop, then read.  Not for concurrent use from several
+ * host threads.
+ */
+typedef enum flce_kernel_kind {
+  FLCE_KERNEL_COMPACT = 0,      /* label compaction                           */
+  FLCE_KERNEL_GATHER = 1,       /* gather of the valid hidden rows            */
+  FLCE_KERNEL_PROJ_LSE = 2,     /* forward projection + softcap + lse partials */
+  FLCE_KERNEL_COMBINE = 3,      /* per-token lse / loss                       */
+  FLCE_KERNEL_FINALIZE = 4,     /* loss reduction                             */
+  FLCE_KERNEL_RECOMPUTE_G = 5,  /* backward logit recompute -> G chunk         */
+  FLCE_KERNEL_DWEIGHT = 6,      /* dW rows of a chunk = G^T X                  */
+  FLCE_KERNEL_DHIDDEN = 7,      /* dH += G W[chunk]                            */
+  FLCE_KERNEL_AUX = 8           /* zero fills, scale, rounding                 */
+} flce_kernel_kind_t;
+
+/*
+ * Start recording up to `capacity` launches (events are created here, so this
+ * call is not for a timed region).  Restarting discards the previous trace.
+ * Errors: FLCE_ERR_INVALID_ARG for capacity <= 0, FLCE_ERR_HIP if events
+ * cannot be created.
+ */
+int flce_trace_start(int capacity);
+
+/* Stop recording; the recorded launches stay readable. */
+int flce_trace_stop(void);
+
+/* Number of launches recorded (at most the capacity). */
+int flce_trace_count(void);
+
+/*
+ * Kind and duration in milliseconds of recorded launch i.
+ * Waits for that launch's end event.  `flops` receives the launch's
+ * algorithmic multiply-add work (2 per multiply-add) for the contraction
+ * kinds, else 0; any output pointer may be NULL.
+ * Errors: FLCE_ERR_INVALID_ARG for i out of range, FLCE_ERR_HIP.
+ */
+int flce_trace_get(int i, int* kind, float* ms, double* flops);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLCE_H */

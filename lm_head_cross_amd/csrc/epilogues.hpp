@@ -1,0 +1,231 @@
+// Epilogues of the tile GEMM: what happens to a 256 x 256 fp32 accumulator
+// tile once its K loop is done.
+#pragma once
+
+#include "gemm_tile.hpp"
+
+namespace flce {
+namespace epi {
+
+using gemm::acc_col;
+using gemm::acc_row;
+
+// Forward: logits tile z^T (rows = head rows v, columns = compacted tokens t).
+// Applies the softcap, drops rows v >= Vu, and reduces each token column to a
+// (max, sum exp(z' - max)) pair for this vocab tile; the tile that holds a
+// token's label also records z'[t, y_t].  (Inkling2 loss page, class
+// description: softcap and cross entropy in fp32, rows past the usable
+// vocabulary never enter the softmax.)
+template <bool CAP>
+struct Lse {
+  struct Params {
+    float2* partials;       // [tiles_v][ldp]
+    int ldp;
+    float* label_logit;     // [Tvp]
+    const int32_t* yc;      // compacted labels [Tvp]
+    const int* tok_count;   // Tv
+    int vocab_limit;        // Vu
+    float softcap, inv_softcap;
+  };
+
+  static __device__ __forceinline__ void apply(const Params& p, f32x16 (&acc)[4][4], int m0, int n0,
+                                               bf16* smem) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int tv = *p.tok_count;
+    float* xchg = reinterpret_cast<float*>(smem);  // [2][256][4]
+
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int tc = acc_col(wn, nb, lane);
+      const int t = n0 + tc;
+      const int y_in = p.yc[t];  // t < Tvp: always inside the buffer
+      const int y = t < tv ? y_in : -1;
+      float zc[64];
+      float mx = kNegInf, lab = 0.0f, found = 0.0f;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int v = m0 + acc_row(wm, mb, r, lane);
+          float z = acc[mb][nb][r];
+          if constexpr (CAP) z = softcap_apply(z, p.softcap, p.inv_softcap);
+          // Rows past the usable vocabulary take no part: -inf drops them
+          // from both the max and the sum.
+          z = v < p.vocab_limit ? z : kNegInf;
+          zc[mb * 16 + r] = z;
+          mx = __builtin_fmaxf(mx, z);
+          lab = v == y ? z : lab;
+          found = v == y ? 1.0f : found;
+        }
+      mx = __builtin_fmaxf(mx, lane_xor32(mx));
+      float s = 0.0f;
+      if (mx != kNegInf) {
+#pragma unroll
+        for (int i = 0; i < 64; ++i) s += exp_e(zc[i] - mx);
+      }
+      s += lane_xor32(s);
+      const float lab2 = lane_xor32(lab);
+      const float found2 = lane_xor32(found);
+      if (found2 != 0.0f) { lab = lab2; found = 1.0f; }
+      if (lane < 32) {
+        float* e = xchg + ((wm * 256 + tc) << 2);
+        e[0] = mx; e[1] = s; e[2] = lab; e[3] = found;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+    // Waves of the top row merge the bottom row's pairs and write out.
+    if (wm == 0 && lane < 32) {
+      const int tile_v = m0 / gemm::BM;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int tc = acc_col(wn, nb, lane);
+        const int t = n0 + tc;
+        if (t >= tv) continue;
+        const float* e0 = xchg + (tc << 2);
+        const float* e1 = xchg + ((256 + tc) << 2);
+        float m = e0[0], s = e0[1];
+        lse_merge(m, s, e1[0], e1[1]);
+        p.partials[(int64_t)tile_v * p.ldp + t] = make_float2(m, s);
+        if (e0[3] != 0.0f) p.label_logit[t] = e0[2];
+        else if (e1[3] != 0.0f) p.label_logit[t] = e1[2];
+      }
+    }
+  }
+};
+
+// Backward recompute: logits tile z^T of one vocabulary chunk (rows = chunk
+// rows, columns = compacted tokens) turned into the logit gradient
+//   G[t, v] = (g/D) (exp(z'[t,v] - lse_t) - [v == y_t]) (1 - (z'/c)^2),
+// rounded to bf16 and stored token-major, G[t][v - chunk start].  Positions
+// past the valid tokens or the chunk get 0.  (chunked_ce page,
+// _ChunkedCrossEntropySum.backward: the fp32 softmax is recomputed.)
+template <bool CAP>
+struct Grad {
+  struct Params {
+    bf16* G;
+    int64_t ldg;
+    int v0;                  // global row of chunk row 0
+    int vw;                  // valid rows in this chunk
+    const float* lse;        // [T], original token order
+    const int32_t* valid_idx;
+    const int32_t* yc;
+    const int* tok_count;
+    const float* scale;      // g / D
+    float softcap, inv_softcap;
+  };
+
+  static __device__ __forceinline__ void apply(const Params& p, f32x16 (&acc)[4][4], int m0, int n0,
+                                               bf16*) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int tv = *p.tok_count;  // > 0: tiles past the valid tokens never get here
+    const float scale = *p.scale;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int t = n0 + acc_col(wn, nb, lane);
+      const bool tok_ok = t < tv;
+      const int ts = tok_ok ? t : 0;
+      const float lse_t = p.lse[p.valid_idx[ts]];
+      const int y_loc = tok_ok ? p.yc[ts] - p.v0 : -1;
+      bf16* grow = p.G + (int64_t)t * p.ldg;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          bf16x4 out;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * q + i;
+            const int m = m0 + acc_row(wm, mb, r, lane);
+            float z = acc[mb][nb][r];
+            if constexpr (CAP) z = softcap_apply(z, p.softcap, p.inv_softcap);
+            float d = exp_e(z - lse_t) - (m == y_loc ? 1.0f : 0.0f);
+            if constexpr (CAP) {
+              const float u = z * p.inv_softcap;
+              d *= 1.0f - u * u;
+            }
+            out[i] = (bf16)((tok_ok && m < p.vw) ? d * scale : 0.0f);
+          }
+          *reinterpret_cast<bf16x4*>(grow + m0 + acc_row(wm, mb, 4 * q, lane)) = out;
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+};
+
+// dW rows of one chunk: plain fp32 store of the rows / columns in range.
+struct StoreF32 {
+  struct Params {
+    float* out;
+    int64_t ldo;
+    int rows, cols;
+  };
+  static __device__ __forceinline__ void apply(const Params& p, f32x16 (&acc)[4][4], int m0, int n0,
+                                               bf16*) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int n = n0 + acc_col(wn, nb, lane);
+      if (n >= p.cols) continue;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + acc_row(wm, mb, r, lane);
+          if (m < p.rows) p.out[(int64_t)m * p.ldo + n] = acc[mb][nb][r];
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+};
+
+// dHidden: fp32 accumulation over the vocabulary chunks in a fixed order; the
+// last chunk rounds to bf16 and writes each compacted token's row back to its
+// original position.
+enum { kAccFirst = 1, kAccLast = 2 };
+struct AccumH {
+  struct Params {
+    float* acc_buf;           // [Tvp][ld] fp32
+    int64_t ld;
+    bf16* dh;                 // [T][ld] bf16
+    const int32_t* valid_idx;
+    const int* tok_count;
+    int cols;
+    int mode;
+  };
+  static __device__ __forceinline__ void apply(const Params& p, f32x16 (&acc)[4][4], int m0, int n0,
+                                               bf16*) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int tv = *p.tok_count;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = m0 + acc_row(wm, mb, r, lane);
+        if (t >= tv) continue;
+        const int64_t orig = (p.mode & kAccLast) ? (int64_t)p.valid_idx[t] : 0;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const int h = n0 + acc_col(wn, nb, lane);
+          if (h >= p.cols) continue;
+          float v = acc[mb][nb][r];
+          const int64_t o = (int64_t)t * p.ld + h;
+          if (!(p.mode & kAccFirst)) v += p.acc_buf[o];
+          if (p.mode & kAccLast) p.dh[orig * p.ld + h] = (bf16)v;
+          else p.acc_buf[o] = v;
+        }
+        if ((r & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      }
+  }
+};
+
+}  // namespace epi
+}  // namespace flce

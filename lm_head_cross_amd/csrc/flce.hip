@@ -1,0 +1,570 @@
+// Fused linear cross-entropy for AMD MI355X (gfx950): the small kernels, the
+// GEMM instantiations and the C ABI declared in include/flce.h.
+//
+// Forward (one stream, no host synchronisation):
+//   compact   labels -> compacted token list (valid_idx, yc) and Tv
+//   gather    Xc[t] = X[valid_idx[t]], zero rows up to the 256-row padding
+//   proj+lse  MFMA tiles of W Xc^T with the softcap / log-sum-exp epilogue
+//   combine   per token: merge the vocab-tile partials in order -> lse, loss
+//   finalize  fixed-order fp64 sum of per-block sums, divided by D
+// Backward:
+//   compact, gather, scale = g / D, zero dH and the padding rows of dW, then
+//   per vocabulary chunk: recompute z^T tiles -> G chunk (bf16), dW rows of
+//   the chunk = G^T Xc, dH_acc += G W[chunk] (the last chunk writes bf16 dH).
+#include <math.h>
+#include <algorithm>
+#include <stdio.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/flce.h"
+#include "epilogues.hpp"
+
+namespace flce {
+
+// ---------------------------------------------------------------------------
+// Small kernels
+// ---------------------------------------------------------------------------
+
+constexpr int kCompactThreads = 1024;
+
+// Stable compaction of the valid positions (label != ignore_index and inside
+// [0, Vu)); an out-of-range label is treated as ignored and flagged.  Also
+// clears the per-token outputs so that ignored positions read 0.
+__global__ __launch_bounds__(kCompactThreads) void k_compact(const int64_t* __restrict__ labels, int T,
+                                                             int Vu, int64_t ignore_index, Meta* meta,
+                                                             int32_t* __restrict__ valid_idx,
+                                                             int32_t* __restrict__ yc, int32_t* status,
+                                                             float* lse_out, float* tl_out) {
+  __shared__ int scan[kCompactThreads];
+  const int tid = threadIdx.x;
+  const int per = (T + kCompactThreads - 1) / kCompactThreads;
+  const int lo = min(tid * per, T);
+  const int hi = min(lo + per, T);
+  int count = 0;
+  int bad = 0;
+  for (int t = lo; t < hi; ++t) {
+    const int64_t y = labels[t];
+    if (lse_out) lse_out[t] = 0.0f;
+    if (tl_out) tl_out[t] = 0.0f;
+    if (y == ignore_index) continue;
+    if (y < 0 || y >= Vu) { bad = 1; continue; }
+    ++count;
+  }
+  if (bad && status) atomicOr(status, FLCE_DEVICE_BAD_LABEL);
+  scan[tid] = count;
+  __syncthreads();
+  for (int off = 1; off < kCompactThreads; off <<= 1) {
+    const int v = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
+  }
+  int pos = scan[tid] - count;
+  if (tid == kCompactThreads - 1) meta->n_valid = scan[tid];
+  for (int t = lo; t < hi; ++t) {
+    const int64_t y = labels[t];
+    if (y == ignore_index || y < 0 || y >= Vu) continue;
+    valid_idx[pos] = t;
+    yc[pos] = (int32_t)y;
+    ++pos;
+  }
+}
+
+// Xc[t, :] = X[valid_idx[t], :] for t < Tv, 0 for Tv <= t < Tvp.
+__global__ __launch_bounds__(256) void k_gather(const uint4* __restrict__ X, int64_t row_vec,
+                                                 const int32_t* __restrict__ valid_idx, const Meta* meta,
+                                                 uint4* __restrict__ Xc, int64_t Tvp) {
+  const int tv = meta->n_valid;
+  const int64_t total = Tvp * row_vec;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = i / row_vec;
+    const int64_t c = i - t * row_vec;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (t < tv) v = X[(int64_t)valid_idx[t] * row_vec + c];
+    Xc[i] = v;
+  }
+}
+
+// Per compacted token: merge the vocab-tile partials in tile order into the
+// log-sum-exp, form the token loss, and reduce the block's losses in fp64.
+__global__ __launch_bounds__(256) void k_combine(const float2* __restrict__ partials, int tiles_v, int ldp,
+                                                  const float* __restrict__ label_logit,
+                                                  const int32_t* __restrict__ valid_idx, const Meta* meta,
+                                                  float* lse_out, float* tl_out, double* block_sums) {
+  __shared__ double red[256];
+  const int tv = meta->n_valid;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  double loss = 0.0;
+  if (t < tv) {
+    float m = kNegInf, s = 0.0f;
+    for (int j = 0; j < tiles_v; ++j) {
+      const float2 pr = partials[(int64_t)j * ldp + t];
+      lse_merge(m, s, pr.x, pr.y);
+    }
+    const float lse = m + log_e(s);
+    const float l = lse - label_logit[t];
+    const int orig = valid_idx[t];
+    lse_out[orig] = lse;
+    if (tl_out) tl_out[orig] = l;
+    loss = (double)l;
+  }
+  red[threadIdx.x] = loss;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) block_sums[blockIdx.x] = red[0];
+}
+
+// Normaliser D: num_label_tokens when given, else Tv for MEAN, else 1.
+__device__ __forceinline__ double divisor(const Meta* meta, int reduction, int64_t num_label_tokens) {
+  if (num_label_tokens > 0) return (double)num_label_tokens;
+  if (reduction == FLCE_REDUCTION_MEAN) return (double)meta->n_valid;
+  return 1.0;
+}
+
+// loss = (fixed-order fp64 sum of the block sums) / D.
+__global__ __launch_bounds__(256) void k_finalize(const double* __restrict__ block_sums, int nblocks,
+                                                   const Meta* meta, int reduction, int64_t num_label_tokens,
+                                                   float* loss) {
+  __shared__ double red[256];
+  double s = 0.0;
+  for (int i = threadIdx.x; i < nblocks; i += 256) s += block_sums[i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *loss = (float)(red[0] / divisor(meta, reduction, num_label_tokens));
+}
+
+// The loss for T == 0: 0 for SUM (or a given count), NaN for MEAN.
+__global__ void k_empty_loss(int reduction, int64_t num_label_tokens, float* loss) {
+  *loss = (num_label_tokens <= 0 && reduction == FLCE_REDUCTION_MEAN) ? __builtin_nanf("") : 0.0f;
+}
+
+__global__ void k_scale(const float* grad_out, const Meta* meta, int reduction, int64_t num_label_tokens,
+                        float* scale) {
+  *scale = (float)((double)*grad_out / divisor(meta, reduction, num_label_tokens));
+}
+
+__global__ __launch_bounds__(256) void k_zero(uint4* __restrict__ p, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__global__ __launch_bounds__(256) void k_round_bf16(const float* __restrict__ src, bf16* __restrict__ dst,
+                                                     int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = (bf16)src[i];
+}
+
+__global__ __launch_bounds__(256) void k_round_bf16_vec(const float4* __restrict__ src, bf16x4* __restrict__ dst,
+                                                         int64_t n4) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += stride) {
+    const float4 v = src[i];
+    bf16x4 o;
+    o[0] = (bf16)v.x; o[1] = (bf16)v.y; o[2] = (bf16)v.z; o[3] = (bf16)v.w;
+    dst[i] = o;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Sizes derived from a validated problem.
+struct Plan {
+  int64_t T, H, V, Vu;
+  int64_t Tvp;          // T rounded up to 256 (the token tile)
+  int64_t tiles_t;      // Tvp / 256
+  int64_t tiles_v;      // ceil(Vu / 256): forward vocab tiles
+  int64_t tiles_h;      // ceil(H / 256)
+  int64_t vc;           // backward vocabulary chunk width (multiple of 256)
+  int64_t nchunks;
+  // workspace byte offsets
+  size_t off_meta, off_valid, off_yc, off_label, off_scale, off_bsum, off_xc;
+  size_t off_part;      // forward region
+  size_t off_g, off_hacc;  // backward region
+  size_t total;
+};
+
+int validate(const flce_problem_t* p) {
+  if (!p) return FLCE_ERR_INVALID_ARG;
+  if (p->num_tokens < 0 || p->hidden <= 0 || p->vocab <= 0) return FLCE_ERR_INVALID_ARG;
+  if (p->unpadded_vocab <= 0 || p->unpadded_vocab > p->vocab) return FLCE_ERR_INVALID_ARG;
+  if (!(p->softcap >= 0.0f) || isinf(p->softcap)) return FLCE_ERR_INVALID_ARG;
+  if (p->reduction != FLCE_REDUCTION_SUM && p->reduction != FLCE_REDUCTION_MEAN) return FLCE_ERR_INVALID_ARG;
+  if (p->num_label_tokens == 0) return FLCE_ERR_INVALID_ARG;
+  if (p->weight_dtype != FLCE_DTYPE_BF16) return FLCE_ERR_UNSUPPORTED;
+  if (p->hidden % 64 != 0) return FLCE_ERR_UNSUPPORTED;
+  // 32-bit token / row / column indices inside the kernels.
+  if (p->num_tokens > (int64_t(1) << 30) || p->vocab > (int64_t(1) << 30) || p->hidden > (int64_t(1) << 20))
+    return FLCE_ERR_UNSUPPORTED;
+  return FLCE_OK;
+}
+
+Plan make_plan(const flce_problem_t* p) {
+  Plan pl{};
+  pl.T = p->num_tokens;
+  pl.H = p->hidden;
+  pl.V = p->vocab;
+  pl.Vu = p->unpadded_vocab;
+  pl.Tvp = align_up((size_t)pl.T, 256);
+  pl.tiles_t = pl.Tvp / 256;
+  pl.tiles_v = ceil_div(pl.Vu, 256);
+  pl.tiles_h = ceil_div(pl.H, 256);
+  // Chunk width: at most a quarter of the usable vocabulary (whole tiles), at
+  // least one tile; chunks of equal width up to the last.
+  const int64_t vc_max = std::max<int64_t>(256, (pl.Vu / 1024) * 256);
+  pl.nchunks = ceil_div(pl.Vu, vc_max);
+  pl.vc = align_up((size_t)ceil_div(pl.Vu, pl.nchunks), 256);
+
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, kAlign); return at; };
+  pl.off_meta = take(sizeof(Meta));
+  pl.off_valid = take(pl.Tvp * 4);
+  pl.off_yc = take(pl.Tvp * 4);
+  pl.off_label = take(pl.Tvp * 4);
+  pl.off_scale = take(16);
+  pl.off_bsum = take(pl.tiles_t * 8);
+  pl.off_xc = take(pl.Tvp * pl.H * 2);
+  const size_t common = o;
+  pl.off_part = take(pl.tiles_v * pl.Tvp * 8);
+  const size_t fwd_end = o;
+  o = common;
+  pl.off_g = take(pl.Tvp * pl.vc * 2);
+  pl.off_hacc = take(pl.nchunks > 1 ? pl.Tvp * pl.H * 4 : 0);
+  const size_t bwd_end = o;
+  pl.total = std::max(fwd_end, bwd_end);
+  return pl;
+}
+
+template <class T>
+T* ws_at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_workspace(const Plan& pl, void* ws, size_t bytes) {
+  if (pl.total == 0) return FLCE_OK;
+  if (!ws || !aligned(ws, kAlign) || bytes < pl.total) return FLCE_ERR_WORKSPACE;
+  return FLCE_OK;
+}
+
+int launch_status() {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    fprintf(stderr, "flce: HIP launch failed: %s\n", hipGetErrorString(e));
+    return FLCE_ERR_HIP;
+  }
+  return FLCE_OK;
+}
+
+// Launch tracing (flce_trace_*): (start, end) event pairs around launches.
+struct Tracer {
+  bool on = false;
+  int cap = 0;
+  int n = 0;
+  std::vector<hipEvent_t> ev;
+  std::vector<int> kind;
+  std::vector<double> flops;
+  void release() {
+    for (hipEvent_t e : ev) hipEventDestroy(e);
+    ev.clear();
+    kind.clear();
+    flops.clear();
+    cap = n = 0;
+    on = false;
+  }
+};
+Tracer g_trace;
+
+// Brackets one launch with trace events when a trace is running.
+struct TraceScope {
+  int slot = -1;
+  hipStream_t s;
+  TraceScope(int kind, double flops, hipStream_t stream) : s(stream) {
+    if (!g_trace.on || g_trace.n >= g_trace.cap) return;
+    slot = g_trace.n++;
+    g_trace.kind[slot] = kind;
+    g_trace.flops[slot] = flops;
+    hipEventRecord(g_trace.ev[2 * slot], s);
+  }
+  ~TraceScope() {
+    if (slot >= 0) hipEventRecord(g_trace.ev[2 * slot + 1], s);
+  }
+};
+
+unsigned grid_for(int64_t n, int64_t per_block, int64_t cap) {
+  int64_t g = ceil_div(n, per_block);
+  if (g < 1) g = 1;
+  if (g > cap) g = cap;
+  return (unsigned)g;
+}
+
+void zero_fill(void* p, int64_t bytes, hipStream_t s) {
+  if (bytes <= 0) return;
+  TraceScope tr(FLCE_KERNEL_AUX, 0.0, s);
+  const int64_t n16 = bytes / 16;
+  hipLaunchKernelGGL(k_zero, dim3(grid_for(n16, 256, 8192)), dim3(256), 0, s, (uint4*)p, n16);
+}
+
+void launch_compact_gather(const Plan& pl, const flce_problem_t& p, const int64_t* labels, const void* hidden,
+                           Meta* meta, int32_t* valid_idx, int32_t* yc, int32_t* device_status, float* lse,
+                           float* token_loss, bf16* xc, hipStream_t stream) {
+  {
+    TraceScope tr(FLCE_KERNEL_COMPACT, 0.0, stream);
+    hipLaunchKernelGGL(k_compact, dim3(1), dim3(kCompactThreads), 0, stream, labels, (int)pl.T, (int)pl.Vu,
+                       p.ignore_index, meta, valid_idx, yc, device_status, lse, token_loss);
+  }
+  const int64_t row_vec = pl.H / 8;
+  TraceScope tr(FLCE_KERNEL_GATHER, 0.0, stream);
+  hipLaunchKernelGGL(k_gather, dim3(grid_for(pl.Tvp * row_vec, 256, 16384)), dim3(256), 0, stream,
+                     (const uint4*)hidden, row_vec, (const int32_t*)valid_idx, (const Meta*)meta, (uint4*)xc,
+                     pl.Tvp);
+}
+
+}  // namespace
+}  // namespace flce
+
+using namespace flce;
+
+extern "C" {
+
+const char* flce_status_string(int status) {
+  switch (status) {
+    case FLCE_OK: return "ok";
+    case FLCE_ERR_INVALID_ARG: return "invalid argument";
+    case FLCE_ERR_UNSUPPORTED: return "unsupported problem";
+    case FLCE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case FLCE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int flce_version(void) { return 100; }
+
+int flce_round_to_bf16(const float* src, void* dst, int64_t count, hipStream_t stream) {
+  if (count < 0) return FLCE_ERR_INVALID_ARG;
+  if (count == 0) return FLCE_OK;
+  if (!src || !dst) return FLCE_ERR_INVALID_ARG;
+  if (!aligned(src, 4) || !aligned(dst, 2)) return FLCE_ERR_UNSUPPORTED;
+  TraceScope tr(FLCE_KERNEL_AUX, 0.0, stream);
+  if (aligned(src, 16) && aligned(dst, 8) && count % 4 == 0) {
+    hipLaunchKernelGGL(k_round_bf16_vec, dim3(grid_for(count / 4, 256, 16384)), dim3(256), 0, stream,
+                       (const float4*)src, (bf16x4*)dst, count / 4);
+  } else {
+    hipLaunchKernelGGL(k_round_bf16, dim3(grid_for(count, 256, 16384)), dim3(256), 0, stream, src, (bf16*)dst,
+                       count);
+  }
+  return launch_status();
+}
+
+int flce_workspace_size(const flce_problem_t* problem, size_t* bytes) {
+  const int st = validate(problem);
+  if (st != FLCE_OK) return st;
+  if (!bytes) return FLCE_ERR_INVALID_ARG;
+  *bytes = problem->num_tokens == 0 ? 0 : make_plan(problem).total;
+  return FLCE_OK;
+}
+
+int flce_forward(const flce_problem_t* problem, const void* hidden, const void* weight, const int64_t* labels,
+                 float* loss, float* lse, float* token_loss, int32_t* device_status, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream) {
+  int st = validate(problem);
+  if (st != FLCE_OK) return st;
+  const flce_problem_t& p = *problem;
+  if (!loss || !weight) return FLCE_ERR_INVALID_ARG;
+  if (p.num_tokens > 0 && (!hidden || !labels || !lse)) return FLCE_ERR_INVALID_ARG;
+  if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(loss, 4) || !aligned(lse, 4) ||
+      !aligned(token_loss, 4) || !aligned(labels, 8) || !aligned(device_status, 4))
+    return FLCE_ERR_UNSUPPORTED;
+  if (p.num_tokens == 0) {
+    TraceScope tr(FLCE_KERNEL_FINALIZE, 0.0, stream);
+    hipLaunchKernelGGL(k_empty_loss, dim3(1), dim3(1), 0, stream, (int)p.reduction, p.num_label_tokens, loss);
+    return launch_status();
+  }
+  const Plan pl = make_plan(&p);
+  if ((st = check_workspace(pl, workspace, workspace_bytes)) != FLCE_OK) return st;
+
+  Meta* meta = ws_at<Meta>(workspace, pl.off_meta);
+  int32_t* valid_idx = ws_at<int32_t>(workspace, pl.off_valid);
+  int32_t* yc = ws_at<int32_t>(workspace, pl.off_yc);
+  float* label_logit = ws_at<float>(workspace, pl.off_label);
+  double* bsum = ws_at<double>(workspace, pl.off_bsum);
+  bf16* xc = ws_at<bf16>(workspace, pl.off_xc);
+  float2* part = ws_at<float2>(workspace, pl.off_part);
+  const int* tv = &meta->n_valid;
+
+  launch_compact_gather(pl, p, labels, hidden, meta, valid_idx, yc, device_status, lse, token_loss, xc, stream);
+  {
+    gemm::Operand A{(const bf16*)weight, pl.H, (int)pl.Vu - 1, 0};
+    gemm::Operand B{xc, pl.H, (int)pl.Tvp - 1, 0};
+    gemm::Schedule sch{(int)pl.tiles_v, (int)pl.tiles_t, (int)(pl.H / gemm::BK), tv, 2};
+    const dim3 grid(pl.tiles_v * pl.tiles_t);
+    TraceScope tr(FLCE_KERNEL_PROJ_LSE, 2.0 * pl.T * pl.Vu * pl.H, stream);
+    if (p.softcap > 0.0f) {
+      epi::Lse<true>::Params ep{part, (int)pl.Tvp, label_logit, yc, tv, (int)pl.Vu, p.softcap, 1.0f / p.softcap};
+      hipLaunchKernelGGL((gemm::gemm_kernel<true, true, epi::Lse<true>>), grid, dim3(gemm::NTHREADS), 0, stream,
+                         A, B, sch, ep);
+    } else {
+      epi::Lse<false>::Params ep{part, (int)pl.Tvp, label_logit, yc, tv, (int)pl.Vu, 0.0f, 0.0f};
+      hipLaunchKernelGGL((gemm::gemm_kernel<true, true, epi::Lse<false>>), grid, dim3(gemm::NTHREADS), 0, stream,
+                         A, B, sch, ep);
+    }
+  }
+  {
+    TraceScope tr(FLCE_KERNEL_COMBINE, 0.0, stream);
+    hipLaunchKernelGGL(k_combine, dim3(pl.tiles_t), dim3(256), 0, stream, (const float2*)part, (int)pl.tiles_v,
+                       (int)pl.Tvp, (const float*)label_logit, (const int32_t*)valid_idx, (const Meta*)meta, lse,
+                       token_loss, bsum);
+  }
+  {
+    TraceScope tr(FLCE_KERNEL_FINALIZE, 0.0, stream);
+    hipLaunchKernelGGL(k_finalize, dim3(1), dim3(256), 0, stream, (const double*)bsum, (int)pl.tiles_t,
+                       (const Meta*)meta, (int)p.reduction, p.num_label_tokens, loss);
+  }
+  return launch_status();
+}
+
+int flce_backward(const flce_problem_t* problem, const void* hidden, const void* weight, const int64_t* labels,
+                  const float* lse, const float* grad_out, void* d_hidden, float* d_weight,
+                  int32_t* device_status, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = validate(problem);
+  if (st != FLCE_OK) return st;
+  const flce_problem_t& p = *problem;
+  if (!weight || !grad_out || !d_weight) return FLCE_ERR_INVALID_ARG;
+  if (p.num_tokens > 0 && (!hidden || !labels || !lse || !d_hidden)) return FLCE_ERR_INVALID_ARG;
+  if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(d_hidden, 16) || !aligned(d_weight, 16) ||
+      !aligned(lse, 4) || !aligned(grad_out, 4) || !aligned(labels, 8) || !aligned(device_status, 4))
+    return FLCE_ERR_UNSUPPORTED;
+  if (p.num_tokens == 0) {
+    zero_fill(d_weight, p.vocab * p.hidden * 4, stream);
+    return launch_status();
+  }
+  const Plan pl = make_plan(&p);
+  if ((st = check_workspace(pl, workspace, workspace_bytes)) != FLCE_OK) return st;
+
+  Meta* meta = ws_at<Meta>(workspace, pl.off_meta);
+  int32_t* valid_idx = ws_at<int32_t>(workspace, pl.off_valid);
+  int32_t* yc = ws_at<int32_t>(workspace, pl.off_yc);
+  float* scale = ws_at<float>(workspace, pl.off_scale);
+  bf16* xc = ws_at<bf16>(workspace, pl.off_xc);
+  bf16* G = ws_at<bf16>(workspace, pl.off_g);
+  float* hacc = ws_at<float>(workspace, pl.off_hacc);
+  const int* tv = &meta->n_valid;
+  const bf16* W = (const bf16*)weight;
+
+  launch_compact_gather(pl, p, labels, hidden, meta, valid_idx, yc, device_status, nullptr, nullptr, xc, stream);
+  {
+    TraceScope tr(FLCE_KERNEL_AUX, 0.0, stream);
+    hipLaunchKernelGGL(k_scale, dim3(1), dim3(1), 0, stream, grad_out, (const Meta*)meta, (int)p.reduction,
+                       p.num_label_tokens, scale);
+  }
+  zero_fill(d_hidden, pl.T * pl.H * 2, stream);
+  zero_fill(d_weight + pl.Vu * pl.H, (pl.V - pl.Vu) * pl.H * 4, stream);
+
+  const float inv_c = p.softcap > 0.0f ? 1.0f / p.softcap : 0.0f;
+  for (int64_t c = 0; c < pl.nchunks; ++c) {
+    const int64_t v0 = c * pl.vc;
+    const int64_t vw = std::min(pl.vc, pl.Vu - v0);
+    const int64_t tiles_c = ceil_div(vw, 256);
+    const bf16* Wc = W + v0 * pl.H;
+    const double chunk_flops = 2.0 * pl.T * vw * pl.H;
+
+    // 1. logits of the chunk -> G (bf16, token-major)
+    {
+      gemm::Operand A{Wc, pl.H, (int)vw - 1, 0};
+      gemm::Operand B{xc, pl.H, (int)pl.Tvp - 1, 0};
+      gemm::Schedule sch{(int)tiles_c, (int)pl.tiles_t, (int)(pl.H / gemm::BK), tv, 2};
+      const dim3 grid(tiles_c * pl.tiles_t);
+      TraceScope tr(FLCE_KERNEL_RECOMPUTE_G, chunk_flops, stream);
+      if (p.softcap > 0.0f) {
+        epi::Grad<true>::Params ep{G, pl.vc, (int)v0, (int)vw, lse, valid_idx, yc, tv, scale, p.softcap, inv_c};
+        hipLaunchKernelGGL((gemm::gemm_kernel<true, true, epi::Grad<true>>), grid, dim3(gemm::NTHREADS), 0,
+                           stream, A, B, sch, ep);
+      } else {
+        epi::Grad<false>::Params ep{G, pl.vc, (int)v0, (int)vw, lse, valid_idx, yc, tv, scale, 0.0f, 0.0f};
+        hipLaunchKernelGGL((gemm::gemm_kernel<true, true, epi::Grad<false>>), grid, dim3(gemm::NTHREADS), 0,
+                           stream, A, B, sch, ep);
+      }
+    }
+    // 2. dW[v0 : v0 + vw] = G^T Xc   (M = chunk rows, N = H, K = tokens)
+    {
+      gemm::Operand A{G, pl.vc, (int)pl.vc - 1, (int)pl.Tvp - 1};
+      gemm::Operand B{xc, pl.H, (int)pl.H - 1, (int)pl.Tvp - 1};
+      gemm::Schedule sch{(int)tiles_c, (int)pl.tiles_h, 0, tv, 3};
+      epi::StoreF32::Params ep{d_weight + v0 * pl.H, pl.H, (int)vw, (int)pl.H};
+      TraceScope tr(FLCE_KERNEL_DWEIGHT, chunk_flops, stream);
+      hipLaunchKernelGGL((gemm::gemm_kernel<false, false, epi::StoreF32>), dim3(tiles_c * pl.tiles_h),
+                         dim3(gemm::NTHREADS), 0, stream, A, B, sch, ep);
+    }
+    // 3. dH_acc (+)= G W[v0 : v0 + vw]   (M = tokens, N = H, K = chunk rows)
+    {
+      gemm::Operand A{G, pl.vc, (int)pl.Tvp - 1, 0};
+      gemm::Operand B{Wc, pl.H, (int)pl.H - 1, (int)vw - 1};
+      gemm::Schedule sch{(int)pl.tiles_t, (int)pl.tiles_h, (int)ceil_div(vw, gemm::BK), tv, 1};
+      int mode = 0;
+      if (c == 0) mode |= epi::kAccFirst;
+      if (c == pl.nchunks - 1) mode |= epi::kAccLast;
+      epi::AccumH::Params ep{hacc, pl.H, (bf16*)d_hidden, valid_idx, tv, (int)pl.H, mode};
+      TraceScope tr(FLCE_KERNEL_DHIDDEN, chunk_flops, stream);
+      hipLaunchKernelGGL((gemm::gemm_kernel<true, false, epi::AccumH>), dim3(pl.tiles_t * pl.tiles_h),
+                         dim3(gemm::NTHREADS), 0, stream, A, B, sch, ep);
+    }
+  }
+  return launch_status();
+}
+
+int flce_trace_start(int capacity) {
+  if (capacity <= 0) return FLCE_ERR_INVALID_ARG;
+  g_trace.release();
+  g_trace.ev.resize(2 * (size_t)capacity, nullptr);
+  for (auto& e : g_trace.ev) {
+    if (hipEventCreate(&e) != hipSuccess) {
+      e = nullptr;
+      g_trace.release();
+      return FLCE_ERR_HIP;
+    }
+  }
+  g_trace.kind.assign(capacity, 0);
+  g_trace.flops.assign(capacity, 0.0);
+  g_trace.cap = capacity;
+  g_trace.n = 0;
+  g_trace.on = true;
+  return FLCE_OK;
+}
+
+int flce_trace_stop(void) {
+  g_trace.on = false;
+  return FLCE_OK;
+}
+
+int flce_trace_count(void) { return g_trace.n; }
+
+int flce_trace_get(int i, int* kind, float* ms, double* flops) {
+  if (i < 0 || i >= g_trace.n) return FLCE_ERR_INVALID_ARG;
+  if (kind) *kind = g_trace.kind[i];
+  if (flops) *flops = g_trace.flops[i];
+  if (ms) {
+    if (hipEventSynchronize(g_trace.ev[2 * i + 1]) != hipSuccess) return FLCE_ERR_HIP;
+    if (hipEventElapsedTime(ms, g_trace.ev[2 * i], g_trace.ev[2 * i + 1]) != hipSuccess) return FLCE_ERR_HIP;
+  }
+  return FLCE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,129 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+header declares, and rejects invalid arguments before any device work.
+
+No call here reaches a kernel launch: each one fails host-side validation
+first (bad problem, null or misaligned pointer, short workspace).  Device
+pointers are never dereferenced on the host, so fake addresses are safe.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from lm_head_cross_amd import _lib
+from lm_head_cross_amd.flce import make_problem
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "flce.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(flce_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_abi():
+    assert _declared_functions() == sorted(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.flce_version() >= 100
+
+
+def test_status_strings():
+    lib = _lib.load()
+    for code in range(5):
+        s = lib.flce_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.flce_status_string(99).decode() == "unknown status"
+
+
+def _ws(problem):
+    lib = _lib.load()
+    out = ctypes.c_size_t(0)
+    code = lib.flce_workspace_size(ctypes.byref(problem), ctypes.byref(out))
+    return code, out.value
+
+
+def test_workspace_size_bounds():
+    # Llama-3-8B head at 4096 tokens: no scratch buffer of logits shape may
+    # exceed a quarter of a bf16 [T, Vu] array.
+    p = make_problem(4096, 4096, 128256)
+    code, ws = _ws(p)
+    assert code == _lib.FLCE_OK
+    full_logits = 4096 * 128256 * 2
+    assert ws < full_logits  # whole workspace below one bf16 [T, V] buffer
+    # padded vocabulary, softcap
+    code, ws3 = _ws(make_problem(8192, 3072, 262144, 256000, softcap=30.0))
+    assert code == _lib.FLCE_OK and ws3 < 8192 * 256000 * 2
+    code, ws0 = _ws(make_problem(0, 128, 1000))
+    assert code == _lib.FLCE_OK and ws0 == 0
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(num_tokens=-1), _lib.FLCE_ERR_INVALID_ARG),
+    (dict(hidden=0), _lib.FLCE_ERR_INVALID_ARG),
+    (dict(vocab=0), _lib.FLCE_ERR_INVALID_ARG),
+    (dict(unpadded_vocab=0), _lib.FLCE_ERR_INVALID_ARG),
+    (dict(unpadded_vocab=1001), _lib.FLCE_ERR_INVALID_ARG),
+    (dict(softcap=-1.0), _lib.FLCE_ERR_INVALID_ARG),
+    (dict(softcap=float("nan")), _lib.FLCE_ERR_INVALID_ARG),
+    (dict(softcap=float("inf")), _lib.FLCE_ERR_INVALID_ARG),
+    (dict(reduction=2), _lib.FLCE_ERR_INVALID_ARG),
+    (dict(num_label_tokens=0), _lib.FLCE_ERR_INVALID_ARG),
+    (dict(hidden=100), _lib.FLCE_ERR_UNSUPPORTED),
+    (dict(weight_dtype=1), _lib.FLCE_ERR_UNSUPPORTED),
+])
+def test_invalid_problem_rejected(kw, expect):
+    p = make_problem(64, 128, 1000)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    code, _ = _ws(p)
+    assert code == expect
+    lib = _lib.load()
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.flce_forward(ctypes.byref(p), fake, fake, fake, fake, fake, None, None, fake, 1 << 30,
+                            None) == expect
+    assert lib.flce_backward(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, None, fake,
+                             1 << 30, None) == expect
+
+
+def test_null_problem():
+    lib = _lib.load()
+    assert lib.flce_workspace_size(None, None) == _lib.FLCE_ERR_INVALID_ARG
+    assert lib.flce_forward(None, None, None, None, None, None, None, None, None, 0, None) == \
+        _lib.FLCE_ERR_INVALID_ARG
+
+
+def test_pointer_and_workspace_checks():
+    lib = _lib.load()
+    p = make_problem(64, 128, 1000)
+    code, need = _ws(p)
+    assert code == 0 and need > 0
+    a = 1 << 24  # fake, aligned device addresses
+    P = ctypes.byref(p)
+    V = ctypes.c_void_p
+    # missing required pointers
+    assert lib.flce_forward(P, V(a), None, V(a), V(a), V(a), None, None, V(a), need, None) == 1
+    assert lib.flce_forward(P, V(a), V(a), V(a), None, V(a), None, None, V(a), need, None) == 1
+    assert lib.flce_forward(P, V(a), V(a), V(a), V(a), None, None, None, V(a), need, None) == 1
+    assert lib.flce_backward(P, V(a), V(a), V(a), V(a), None, V(a), V(a), None, V(a), need, None) == 1
+    # misaligned operands
+    assert lib.flce_forward(P, V(a + 2), V(a), V(a), V(a), V(a), None, None, V(a), need, None) == 2
+    assert lib.flce_forward(P, V(a), V(a + 8), V(a), V(a), V(a), None, None, V(a), need, None) == 2
+    # workspace: missing, misaligned, short
+    assert lib.flce_forward(P, V(a), V(a), V(a), V(a), V(a), None, None, None, need, None) == 3
+    assert lib.flce_forward(P, V(a), V(a), V(a), V(a), V(a), None, None, V(a + 64), need, None) == 3
+    assert lib.flce_forward(P, V(a), V(a), V(a), V(a), V(a), None, None, V(a), need - 1, None) == 3
+    assert lib.flce_backward(P, V(a), V(a), V(a), V(a), V(a), V(a), V(a), None, V(a), need - 1, None) == 3
+
+
+def test_python_binding_argument_errors():
+    with pytest.raises(ValueError):
+        make_problem(4, 128, 10, reduction="none")
+    with pytest.raises(ValueError):
+        make_problem(4, 128, 10, num_label_tokens=-3)

@@ -1,0 +1,227 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Small shapes are compared element by element over every output; they span
+several 256-wide tiles in every dimension with ragged tails, and several
+vocabulary chunks in the backward pass.  The five named workloads run at
+full size and are checked on every token's loss, the total loss, and dX /
+dW on seeded subsets of >= 512 tokens and >= 512 vocabulary rows (the lse of
+every token comes from the oracle, stored by tests/golden/make_oracle_lse.py).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_common import (TOL_GRAD_REL_L2, TOL_TOKEN_ABS, TOL_TOTAL_REL, check_full, oracle_problem,
+                              rel_l2, run_hip, say, stored_lse)
+from workloads import WORKLOADS, Workload, make_inputs, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _small(key, **kw):
+    base = dict(name=f"case{key}", x_std=1.0, w_std=0.05)
+    base.update(kw)
+    return Workload(key=key, **base)
+
+
+SMALL = {
+    "tiny": WORKLOADS[1],
+    "ragged_softcap_mean_pad": _small(101, T=600, H=320, V=1300, Vu=1100, w_std=0.3, pad_std=30.0,
+                                      softcap=7.0, reduction="mean", ignore_frac=0.1),
+    "multichunk_sum_runs": _small(102, T=1000, H=512, V=3000, Vu=3000, w_std=2.0 / math.sqrt(512),
+                                  ignore="runs"),
+    "count_normalised": _small(103, T=777, H=192, V=2100, Vu=2049, w_std=0.1, softcap=30.0,
+                               ignore_frac=0.3, normalise_by_count=True),
+    "peaked": _small(104, T=300, H=256, V=4099, Vu=4099, w_std=0.4, softcap=30.0, ignore_frac=0.02,
+                     labels="argmax70"),
+    "fp32_head": _small(105, T=513, H=128, V=1536, Vu=1500, w_std=0.2, head_fp32=True, softcap=30.0,
+                        ignore_frac=0.05),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_full_parity(name):
+    w = SMALL[name]
+    say(f"case {name}: T={w.T} H={w.H} V={w.V} Vu={w.Vu} c={w.softcap} {w.reduction}")
+    inp = make_inputs(w, argmax_device="cuda:0")
+    res = run_hip(inp)
+    assert res["status"] == 0
+    check_full(inp, res, label=name)
+
+
+def test_grad_out_scaling():
+    w = SMALL["ragged_softcap_mean_pad"]
+    inp = make_inputs(w)
+    res = run_hip(inp, grad_out=-2.5)
+    check_full(inp, res, grad_out=-2.5, label="grad_out=-2.5")
+
+
+def test_deterministic_repeat():
+    inp = make_inputs(SMALL["multichunk_sum_runs"])
+    a = run_hip(inp)
+    b = run_hip(inp)
+    assert a["loss"] == b["loss"]
+    for k in ("lse", "token_loss", "dX", "dW"):
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_padding_rows_never_read():
+    """NaN in the head rows past unpadded_vocab changes nothing, bit for bit."""
+    inp = make_inputs(SMALL["ragged_softcap_mean_pad"])
+    a = run_hip(inp)
+    poisoned = dict(inp)
+    W = inp["weight"].clone()
+    W[inp["unpadded_vocab"]:] = float("nan")
+    poisoned["weight"] = W
+    b = run_hip(poisoned)
+    assert a["loss"] == b["loss"]
+    for k in ("lse", "token_loss", "dX", "dW"):
+        assert torch.equal(a[k], b[k]), k
+    assert torch.all(b["dW"][inp["unpadded_vocab"]:] == 0)
+
+
+def _custom(inp, labels, **kw):
+    out = dict(inp)
+    out["labels"] = torch.as_tensor(labels, dtype=torch.int64)
+    out.update(kw)
+    return out
+
+
+@pytest.mark.parametrize("reduction", ["sum", "mean"])
+def test_all_positions_ignored(reduction):
+    inp = make_inputs(WORKLOADS[1])
+    T = inp["hidden"].shape[0]
+    c = _custom(inp, np.full(T, -100), reduction=reduction)
+    res = run_hip(c)
+    if reduction == "sum":
+        assert res["loss"] == 0.0
+    else:
+        assert math.isnan(res["loss"])
+    assert torch.all(res["dX"] == 0) and torch.all(res["dW"] == 0)
+    assert torch.all(res["lse"] == 0) and torch.all(res["token_loss"] == 0)
+
+
+def test_single_token_and_vocab_edges():
+    inp = make_inputs(SMALL["ragged_softcap_mean_pad"])
+    T = inp["hidden"].shape[0]
+    Vu = inp["unpadded_vocab"]
+    lab = np.full(T, -100)
+    lab[T - 1] = Vu - 1
+    res = run_hip(_custom(inp, lab))
+    check_full(_custom(inp, lab), res, label="single token, last usable row")
+    lab = np.full(T, -100)
+    lab[0] = 0
+    lab[255] = 255
+    lab[256] = 256
+    lab[T - 1] = Vu - 1
+    check_full(_custom(inp, lab), run_hip(_custom(inp, lab)), label="tile edges")
+
+
+def test_one_token_problem():
+    inp = make_inputs(WORKLOADS[1])
+    one = dict(inp)
+    one["hidden"] = inp["hidden"][5:6].contiguous()
+    one["labels"] = torch.tensor([17])
+    check_full(one, run_hip(one), label="T=1")
+
+
+def test_ignore_index_inside_vocabulary():
+    inp = make_inputs(WORKLOADS[1])
+    lab = inp["labels"].numpy().copy()
+    lab[lab == -100] = 3
+    lab[:5] = 3
+    c = _custom(inp, lab, ignore_index=3)
+    check_full(c, run_hip(c), label="ignore_index=3")
+
+
+def test_out_of_range_labels_flagged_and_skipped():
+    inp = make_inputs(WORKLOADS[1])
+    lab = inp["labels"].numpy().copy()
+    bad = lab.copy()
+    bad[[1, 7]] = [1000, -5]
+    res = run_hip(_custom(inp, bad))
+    assert res["status"] == 1
+    ref = lab.copy()
+    ref[[1, 7]] = -100
+    check_full(_custom(inp, ref), res, label="bad labels as ignored")
+
+
+def test_empty_batch():
+    import lm_head_cross_amd as L
+    d = torch.device("cuda:0")
+    p = L.make_problem(0, 128, 1000, reduction="mean")
+    X = torch.empty((0, 128), dtype=torch.bfloat16, device=d)
+    W = torch.randn(1000, 128, device=d).to(torch.bfloat16)
+    y = torch.empty(0, dtype=torch.int64, device=d)
+    loss = torch.zeros((), device=d)
+    lse = torch.empty(0, device=d)
+    L.flce_forward(p, X, W, y, loss, lse)
+    dW = torch.full((1000, 128), 7.0, device=d)
+    L.flce_backward(p, X, W, y, lse, torch.ones((), device=d), torch.empty_like(X), dW)
+    torch.cuda.synchronize()
+    assert math.isnan(loss.item())
+    assert torch.all(dW == 0)
+
+
+def test_round_to_bf16_matches_oracle_rounding():
+    import lm_head_cross_amd as L
+    rng = np.random.default_rng(3)
+    a = np.concatenate([rng.standard_normal(100003).astype(np.float32),
+                        ((rng.integers(0, 0x7F7F, 5000, dtype=np.uint32) << 16) | 0x8000).view(np.float32),
+                        np.array([0.0, -0.0, np.inf, -np.inf, 3.4e38, -3.4e38, 1e-40], dtype=np.float32)])
+    for arr in (a, a[:100001]):  # vector and scalar kernel paths
+        src = torch.from_numpy(arr.copy()).to("cuda:0")
+        got = L.flce_round_to_bf16(src).cpu().double().numpy()
+        assert np.array_equal(got, oracle.round_fp32_to_bf16(arr))
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads, sampled checks
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("key", [2, 3, 4, 5])
+def test_workload_full_size(key):
+    w = WORKLOADS[key]
+    say(f"workload {key}: {w.name}")
+    inp = make_inputs(w, argmax_device="cuda:0")
+    y = inp["labels"].numpy()
+    tok, voc = sample_rows(w, y)
+    res = run_hip(inp, dx_rows=tok, dw_rows=voc, keep_device=True)
+    assert res["status"] == 0
+    if w.V > w.Vu:
+        assert res["dW_dev"][w.Vu:].abs().max().item() == 0.0
+    valid = y != -100
+    assert torch.all(res["dX_dev"][torch.from_numpy(~valid).to("cuda:0")] == 0)
+    del res["dW_dev"], res["dX_dev"]
+    torch.cuda.empty_cache()
+
+    X = oracle.to_f64(inp["hidden"])
+    W = oracle.head_values(inp["weight"])[: w.Vu]
+    p = oracle_problem(inp)
+    D = oracle.divisor(p, int(valid.sum()))
+    lse_all = stored_lse(key)
+    ll = oracle.label_logits(X, W, y, p)
+    ref_tl = np.where(valid, lse_all - ll, 0.0)
+    ref_loss = math.fsum(ref_tl.tolist()) / D
+    tl_err = np.abs(res["token_loss"].double().numpy() - ref_tl).max()
+    say(f"  loss gpu={res['loss']:.9g} ref={ref_loss:.9g} rel={abs(res['loss'] - ref_loss) / abs(ref_loss):.3g}"
+        f" max|dl|={tl_err:.3g}")
+    assert tl_err <= TOL_TOKEN_ABS
+    assert abs(res["loss"] - ref_loss) <= TOL_TOTAL_REL * abs(ref_loss)
+    lse_gpu = res["lse"].double().numpy()
+    assert np.abs(lse_gpu[valid] - lse_all[valid]).max() <= TOL_TOKEN_ABS
+
+    tl_s, lse_s, dX_s = oracle.token_rows(X, W, y, tok, p, D)
+    # The stored lse must be the live oracle's (same inputs on this machine).
+    vs = valid[tok]
+    np.testing.assert_allclose(lse_s[vs], lse_all[tok][vs], rtol=1e-12)
+    e_dx = rel_l2(res["dX"].double().numpy(), dX_s)
+    dW_r = oracle.weight_rows(X, W, y, voc, lse_all, p, D)
+    e_dw = rel_l2(res["dW"].double().numpy(), dW_r)
+    say(f"  dX relL2 over {len(tok)} rows = {e_dx:.3g}; dW relL2 over {len(voc)} rows = {e_dw:.3g}")
+    assert e_dx <= TOL_GRAD_REL_L2
+    assert e_dw <= TOL_GRAD_REL_L2

@@ -140,19 +140,10 @@ def _argmax_labels(X: torch.Tensor, W: torch.Tensor, Vu: int, device) -> np.ndar
     return torch.cat(out).numpy().astype(np.int64)
 
 
-def make_inputs(key_or_workload, device="cpu", argmax_device=None):
-    """Draw one workload's inputs.
-
-    Returns a dict with ``hidden`` (bf16 [T,H]), ``weight`` (bf16 [V,H], or
-    fp32 when the workload hands the head over in fp32), ``labels`` (int64 [T])
-    and the workload's loss knobs.  Tensors are placed on ``device``.
-    ``argmax_device`` is where peaked labels are searched (default: ``device``).
-    """
-    w = key_or_workload if isinstance(key_or_workload, Workload) else WORKLOADS[key_or_workload]
-    root = np.random.SeedSequence(w.seed)
-    sx, sw, srest = root.spawn(3)
-    rng = np.random.Generator(np.random.PCG64(srest))
-
+def draw_hidden_and_head(w: Workload):
+    """Hidden states (bf16 [T,H]) and head (bf16, or fp32 when the workload
+    hands it over in fp32, [V,H]) of one workload, on the CPU."""
+    sx, sw, _ = np.random.SeedSequence(w.seed).spawn(3)
     X = torch.from_numpy(_normal_f32((w.T, w.H), sx, w.x_std)).to(torch.bfloat16)
     Wf = _normal_f32((w.V, w.H), sw, w.w_std)
     if w.V > w.Vu:
@@ -162,7 +153,20 @@ def make_inputs(key_or_workload, device="cpu", argmax_device=None):
     Wt = torch.from_numpy(Wf)
     if not w.head_fp32:
         Wt = Wt.to(torch.bfloat16)
-    del Wf
+    return X, Wt
+
+
+def make_inputs(key_or_workload, device="cpu", argmax_device=None):
+    """Draw one workload's inputs.
+
+    Returns a dict with ``hidden`` (bf16 [T,H]), ``weight`` (bf16 [V,H], or
+    fp32 when the workload hands the head over in fp32), ``labels`` (int64 [T])
+    and the workload's loss knobs.  Tensors are placed on ``device``.
+    ``argmax_device`` is where peaked labels are searched (default: ``device``).
+    """
+    w = key_or_workload if isinstance(key_or_workload, Workload) else WORKLOADS[key_or_workload]
+    X, Wt = draw_hidden_and_head(w)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(w.seed).spawn(3)[2]))
 
     ignored = _ignore_mask(w, rng)
     labels = rng.integers(0, w.Vu, size=w.T, dtype=np.int64)
