@@ -80,7 +80,7 @@ typedef enum flce_dtype {
  * Problem description, shared by every entry point.
  *
  * num_tokens        T >= 0: flattened [batch, sequence] positions.
- * hidden            H > 0, a multiple of 64.
+ * hidden            H > 0, a multiple of 128.
  * vocab             V: rows of the head, padding included.
  * unpadded_vocab    Vu, 0 < Vu <= V: rows that take part in the softmax
  *                   (Inkling2 page, constructor argument unpadded_vocab_size).

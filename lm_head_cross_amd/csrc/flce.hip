@@ -211,7 +211,7 @@ int validate(const flce_problem_t* p) {
   if (p->reduction != FLCE_REDUCTION_SUM && p->reduction != FLCE_REDUCTION_MEAN) return FLCE_ERR_INVALID_ARG;
   if (p->num_label_tokens == 0) return FLCE_ERR_INVALID_ARG;
   if (p->weight_dtype != FLCE_DTYPE_BF16) return FLCE_ERR_UNSUPPORTED;
-  if (p->hidden % 64 != 0) return FLCE_ERR_UNSUPPORTED;
+  if (p->hidden % 128 != 0) return FLCE_ERR_UNSUPPORTED;
   // 32-bit token / row / column indices inside the kernels.
   if (p->num_tokens > (int64_t(1) << 30) || p->vocab > (int64_t(1) << 30) || p->hidden > (int64_t(1) << 20))
     return FLCE_ERR_UNSUPPORTED;
@@ -308,6 +308,13 @@ struct TraceScope {
     if (slot >= 0) hipEventRecord(g_trace.ev[2 * slot + 1], s);
   }
 };
+
+// K steps of BK for a K extent, padded to whole groups of NST stages (the
+// operands are zero, or multiplied by zero, in the padding).
+int k_steps_for(int64_t K) {
+  const int64_t group = (int64_t)gemm::NST * gemm::BK;
+  return (int)(ceil_div(K, group) * gemm::NST);
+}
 
 unsigned grid_for(int64_t n, int64_t per_block, int64_t cap) {
   int64_t g = ceil_div(n, per_block);
@@ -414,7 +421,7 @@ int flce_forward(const flce_problem_t* problem, const void* hidden, const void* 
   {
     gemm::Operand A{(const bf16*)weight, pl.H, (int)pl.Vu - 1, 0};
     gemm::Operand B{xc, pl.H, (int)pl.Tvp - 1, 0};
-    gemm::Schedule sch{(int)pl.tiles_v, (int)pl.tiles_t, (int)(pl.H / gemm::BK), tv, 2};
+    gemm::Schedule sch{(int)pl.tiles_v, (int)pl.tiles_t, k_steps_for(pl.H), tv, 2};
     const dim3 grid(pl.tiles_v * pl.tiles_t);
     TraceScope tr(FLCE_KERNEL_PROJ_LSE, 2.0 * pl.T * pl.Vu * pl.H, stream);
     if (p.softcap > 0.0f) {
@@ -490,7 +497,7 @@ int flce_backward(const flce_problem_t* problem, const void* hidden, const void*
     {
       gemm::Operand A{Wc, pl.H, (int)vw - 1, 0};
       gemm::Operand B{xc, pl.H, (int)pl.Tvp - 1, 0};
-      gemm::Schedule sch{(int)tiles_c, (int)pl.tiles_t, (int)(pl.H / gemm::BK), tv, 2};
+      gemm::Schedule sch{(int)tiles_c, (int)pl.tiles_t, k_steps_for(pl.H), tv, 2};
       const dim3 grid(tiles_c * pl.tiles_t);
       TraceScope tr(FLCE_KERNEL_RECOMPUTE_G, chunk_flops, stream);
       if (p.softcap > 0.0f) {
@@ -517,7 +524,7 @@ int flce_backward(const flce_problem_t* problem, const void* hidden, const void*
     {
       gemm::Operand A{G, pl.vc, (int)pl.Tvp - 1, 0};
       gemm::Operand B{Wc, pl.H, (int)pl.H - 1, (int)vw - 1};
-      gemm::Schedule sch{(int)pl.tiles_t, (int)pl.tiles_h, (int)ceil_div(vw, gemm::BK), tv, 1};
+      gemm::Schedule sch{(int)pl.tiles_t, (int)pl.tiles_h, k_steps_for(vw), tv, 1};
       int mode = 0;
       if (c == 0) mode |= epi::kAccFirst;
       if (c == pl.nchunks - 1) mode |= epi::kAccLast;

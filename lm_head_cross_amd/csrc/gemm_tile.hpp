@@ -4,24 +4,35 @@
 // One workgroup of 256 threads (4 wave64s arranged 2 x 2) owns a 256 x 256
 // output tile; each wave owns 128 x 128 of it as 4 x 4 blocks of the
 // v_mfma_f32_32x32x16_bf16 instruction, whose fp32 accumulators live in the
-// AGPR half of the register file.  The K dimension advances 64 at a time
-// through two LDS stages (2 operands x 32 KB each per stage, 128 KB total),
-// filled by global_load_lds_dwordx4: the load unit writes each lane's 16 bytes
-// straight into LDS, so staging uses no VGPRs and no LDS write instructions.
+// AGPR half of the register file (one wave per SIMD).
+//
+// K advances 32 at a time through four LDS stages of 32 KB (A and B tiles of
+// 16 KB each), each its own __shared__ array.  Stages are filled by
+// global_load_lds_dwordx4, which writes each lane's 16 bytes straight into
+// LDS (no VGPR staging, no LDS write instructions), three stages ahead of the
+// stage being multiplied.  Separate arrays let the compiler see that a DMA in
+// flight never aliases the stage being read, so it does not stall LDS reads
+// on it; the wait before each workgroup barrier names how many DMA
+// instructions may still be outstanding.
+//
+// Within a stage, the MFMA fragments of the next 16-wide k step are read
+// while the current step's 16 MFMAs issue.  The barrier that hands the next
+// stage over sits before the last k step's MFMAs, so those MFMAs cover the
+// barrier and the first LDS reads of the next stage.
 //
 // Either operand may be K-major (element (mn, k) at ptr[mn*ld + k]) or
 // MN-major (element (mn, k) at ptr[k*ld + mn]); the LDS tile keeps the
-// global layout, so loads stay fully coalesced either way:
-//  - K-major tile: 256 rows x 64 k (128-byte rows).  An MFMA fragment (one
-//    row, 8 consecutive k) is one ds_read_b128.  The 16-byte chunk c of row r
-//    sits at chunk c ^ swz_k(r), which spreads the 16 (or 8) lanes that the
-//    LDS services together over distinct banks.
-//  - MN-major tile: 64 k-rows x 256 mn (512-byte rows).  A fragment is built
-//    from two ds_read_b64_tr_b16: within each 16-lane group the hardware
-//    transposes a 4 (k) x 16 (mn) block so that lane i receives column i,
-//    four consecutive k.  Chunk pairs are XOR-swizzled per k-row so the four
-//    rows one group reads, and the two groups of a half-wave, hit distinct
-//    banks.
+// global layout, so global loads stay fully coalesced either way:
+//  - K-major tile: 256 rows x 32 k (64-byte rows).  A fragment (one row,
+//    8 consecutive k) is one ds_read_b128.  The 16-byte chunk c of row r sits
+//    at chunk c ^ swz_k(r), so the lanes the LDS services together (16 per
+//    cycle with 64 banks, 8 with 32) hit distinct banks.
+//  - MN-major tile: 32 k-rows x 256 mn (512-byte rows).  A fragment is two
+//    ds_read_b64_tr_b16: within each 16-lane group the hardware transposes a
+//    4 (k) x 16 (mn) block so that lane i receives column i, four
+//    consecutive k.  Pairs of 16-byte chunks are XOR-swizzled per k-row so
+//    the four rows a group reads, and the two groups of a half-wave, hit
+//    distinct banks.
 //
 // The accumulator layout of the 32x32 MFMA: lane l, register r holds element
 // (row 8*(r/4) + 4*(l/32) + r%4, column l%32) of its block.
@@ -34,11 +45,14 @@ namespace gemm {
 
 constexpr int BM = 256;
 constexpr int BN = 256;
-constexpr int BK = 64;
+constexpr int BK = 32;
+constexpr int NST = 4;                        // LDS stages
+constexpr int SUB = BK / 16;                  // MFMA k steps per stage
 constexpr int NTHREADS = 256;
-constexpr int TILE_ELEMS = 256 * BK;          // one operand, one stage
-constexpr int STAGE_ELEMS = 2 * TILE_ELEMS;   // A + B
-constexpr int SMEM_ELEMS = 2 * STAGE_ELEMS;   // two stages: 128 KB
+constexpr int TILE_ELEMS = 256 * BK;          // one operand, one stage (16 KB)
+constexpr int STAGE_ELEMS = 2 * TILE_ELEMS;   // A + B (32 KB)
+constexpr int LOADS_PER_STAGE = STAGE_ELEMS * 2 / 16 / NTHREADS;  // DMA instructions per thread (8)
+constexpr int LOADS_PER_TILE = LOADS_PER_STAGE / 2;               // per operand (4)
 
 // One GEMM operand.
 struct Operand {
@@ -51,12 +65,12 @@ struct Operand {
 // Tile bookkeeping shared by every GEMM launch.
 struct Schedule {
   int tiles_m, tiles_n;
-  int k_steps;              // K / BK when the K extent is known on the host
+  int k_steps;              // K / BK (a multiple of NST) when K is known on the host
   const int* tok_count;     // device count of valid tokens (may be null)
   int tok_dim;              // 0: none, 1: M is tokens, 2: N is tokens, 3: K is tokens
 };
 
-__device__ __forceinline__ int swz_k(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ __forceinline__ int swz_k(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
 // Chunk XOR for MN-major rows: pairs of 16-byte chunks are XOR-ed with
 // t(k % 4) in {0, 3, 5, 6}; t and t ^ 1 cover all eight pair slots of 256 B.
@@ -66,35 +80,83 @@ __device__ __forceinline__ void lds_dma16(const bf16* src, bf16* lds_dst) {
   __builtin_amdgcn_global_load_lds((const void*)src, (FLCE_LDS void*)lds_dst, 16, 0, 0);
 }
 
-// Stage one 256 (mn) x 64 (k) K-major tile: 32 KB = 32 wave-instructions of
-// 1 KB (8 rows), 8 per wave.
-__device__ __forceinline__ void load_tile_kmajor(const Operand& op, int mn0, int k0, bf16* dst,
-                                                 int wave, int lane) {
-  const bf16* base = op.ptr + (int64_t)k0;
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int b = wave * 8 + q;
-    const int r = b * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ swz_k(r);
-    const int gr = min(mn0 + r, op.mn_max);
-    lds_dma16(base + (int64_t)gr * op.ld + c * 8, dst + b * 512);
-  }
+// s_waitcnt with vmcnt <= n (n < 64) and lgkmcnt = 0 (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
 
-// Stage one 64 (k) x 256 (mn) MN-major tile: 32 wave-instructions of 1 KB
-// (2 k-rows of 512 B), 8 per wave.
-__device__ __forceinline__ void load_tile_mnmajor(const Operand& op, int mn0, int k0, bf16* dst,
-                                                  int wave, int lane) {
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int b = wave * 8 + q;
-    const int kk = b * 2 + (lane >> 5);
-    const int c = (lane & 31) ^ swz_mn(kk);
-    const int gk = min(k0 + kk, op.k_max);
-    const int col = min(mn0 + c * 8, op.mn_max - 7);
-    lds_dma16(op.ptr + (int64_t)gk * op.ld + col, dst + b * 512);
-  }
+// Workgroup barrier after this wave's DMA instructions older than the newest
+// `n_out` have landed and its LDS reads are done.  A fence-based barrier
+// would also wait for the DMAs still in flight into the other stages.
+template <int N_OUT>
+__device__ __forceinline__ void stage_barrier() {
+  wait_vm_lgkm0<N_OUT>();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
+
+// Per-thread DMA sources for one operand: a uniform base and per-lane
+// offsets that do not change along K (a K tail is clamped separately).
+template <bool KMAJOR>
+struct Loader {
+  const bf16* base;        // uniform
+  int64_t ld;
+  int k_max;
+  int off[LOADS_PER_TILE]; // elements from base (+ k0 or k0*ld)
+  int kk[LOADS_PER_TILE];  // MN-major: k row within the stage
+  int col[LOADS_PER_TILE]; // MN-major: column offset within the row
+
+  __device__ __forceinline__ Loader(const Operand& op, int mn0, int wave, int lane) {
+    ld = op.ld;
+    k_max = op.k_max;
+    if constexpr (KMAJOR) {
+      base = op.ptr + (int64_t)mn0 * op.ld;
+#pragma unroll
+      for (int q = 0; q < LOADS_PER_TILE; ++q) {
+        const int b = wave * LOADS_PER_TILE + q;   // 1 KB block: 16 rows of 64 B
+        const int r = b * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ swz_k(r);
+        const int gr = min(mn0 + r, op.mn_max) - mn0;
+        off[q] = gr * (int)op.ld + c * 8;
+        kk[q] = 0;
+        col[q] = 0;
+      }
+    } else {
+      base = op.ptr;
+#pragma unroll
+      for (int q = 0; q < LOADS_PER_TILE; ++q) {
+        const int b = wave * LOADS_PER_TILE + q;   // 1 KB block: 2 k-rows of 512 B
+        kk[q] = b * 2 + (lane >> 5);
+        const int c = (lane & 31) ^ swz_mn(kk[q]);
+        col[q] = min(mn0 + c * 8, op.mn_max - 7);
+        off[q] = kk[q] * (int)op.ld + col[q];
+      }
+    }
+  }
+
+  // Issue this thread's share of the stage starting at k0 into `tile`.
+  // MN-major rows past k_max are clamped to it (their partner operand is
+  // zero there); K-major operands are read in full rows of padded K.
+  __device__ __forceinline__ void issue(bf16* tile, int k0, int wave) const {
+    if constexpr (KMAJOR) {
+      const bf16* src = base + k0;
+#pragma unroll
+      for (int q = 0; q < LOADS_PER_TILE; ++q)
+        lds_dma16(src + off[q], tile + (wave * LOADS_PER_TILE + q) * 512);
+    } else {
+      const bf16* src = base + (int64_t)k0 * ld;
+      const int krem = k_max - k0;
+#pragma unroll
+      for (int q = 0; q < LOADS_PER_TILE; ++q) {
+        const int kr = min(kk[q], krem);
+        lds_dma16(src + (kr * (int)ld + col[q]), tile + (wave * LOADS_PER_TILE + q) * 512);
+      }
+    }
+  }
+};
 
 // Fragment of a K-major tile: row `row` (0..255), k = 16*s + 8*(lane/32) + 0..7.
 __device__ __forceinline__ bf16x8 frag_kmajor(const bf16* tile, int row, int s, int lane) {
@@ -108,14 +170,38 @@ __device__ __forceinline__ bf16x8 frag_mnmajor(const bf16* tile, int col0, int s
   const int g = lane >> 4;
   const int j = lane & 15;
   const int col = col0 + 16 * (g & 1) + 4 * (j & 3);
-  const int kb = 16 * s + 8 * (g >> 1) + (j >> 2);
-  const int k0 = kb;
-  const int k1 = kb + 4;
+  const int k0 = 16 * s + 8 * (g >> 1) + (j >> 2);
+  const int k1 = k0 + 4;
   const bf16* p0 = tile + k0 * 256 + (((col >> 3) ^ swz_mn(k0)) << 3) + (col & 7);
   const bf16* p1 = tile + k1 * 256 + (((col >> 3) ^ swz_mn(k1)) << 3) + (col & 7);
   const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((FLCE_LDS bf16x4*)p0);
   const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((FLCE_LDS bf16x4*)p1);
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <bool A_KMAJOR, bool B_KMAJOR>
+__device__ __forceinline__ void read_frags(const bf16* stage, int s, int wm, int wn, int lane, bf16x8 (&fa)[4],
+                                           bf16x8 (&fb)[4]) {
+  const bf16* sa = stage;
+  const bf16* sb = stage + TILE_ELEMS;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (A_KMAJOR) fa[i] = frag_kmajor(sa, wm * 128 + 32 * i + (lane & 31), s, lane);
+    else fa[i] = frag_mnmajor(sa, wm * 128 + 32 * i, s, lane);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (B_KMAJOR) fb[i] = frag_kmajor(sb, wn * 128 + 32 * i + (lane & 31), s, lane);
+    else fb[i] = frag_mnmajor(sb, wn * 128 + 32 * i, s, lane);
+  }
+}
+
+__device__ __forceinline__ void mfma_step(const bf16x8 (&fa)[4], const bf16x8 (&fb)[4], f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
 }
 
 // Map a workgroup id to a tile so that the workgroups one XCD runs (ids that
@@ -130,11 +216,70 @@ __device__ __forceinline__ void tile_of(int pid, int tiles_m, int tiles_n, int& 
   tn = logical - tm * tiles_n;
 }
 
-// The main loop.  acc[mb][nb] is the 32x32 block at rows wm*128 + 32*mb,
-// columns wn*128 + 32*nb of the tile.
+// LDS read instructions one read_frags issues.
 template <bool A_KMAJOR, bool B_KMAJOR>
-__device__ __forceinline__ void mainloop(const Operand& A, const Operand& B, int m0, int n0,
-                                         int k_steps, bf16* smem, f32x16 (&acc)[4][4]) {
+constexpr int frag_reads() { return (A_KMAJOR ? 4 : 8) + (B_KMAJOR ? 4 : 8); }
+
+// Scheduling masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedVmemRead = 0x020;
+constexpr int kSchedDsRead = 0x100;
+
+// One stage of the main loop: the MFMA k steps of stage `cur`, with the
+// hand-over to stage `nxt` before the last step.  WAIT_OUT is the number of
+// this thread's DMA instructions that may still be in flight at the barrier
+// (the stages issued after `nxt`); REFILL issues stage `refill_step` into
+// `cur` once every wave is done reading it; LAST skips the hand-over.
+//
+// Instruction order is pinned per k step: the next step's LDS reads are
+// spread between this step's 16 MFMAs, so their latency hides behind the
+// MFMAs instead of stalling them.  After the hand-over barrier the next
+// stage's first reads go out first, then the refill DMAs between MFMAs.
+template <bool A_KMAJOR, bool B_KMAJOR, int WAIT_OUT, bool REFILL, bool LAST, class DMA>
+__device__ __forceinline__ void stage_compute(bf16* cur, bf16* nxt, int refill_step, const DMA& dma, int wm, int wn,
+                                              int lane, bf16x8 (&fa)[2][4], bf16x8 (&fb)[2][4],
+                                              f32x16 (&acc)[4][4]) {
+  constexpr int NR = frag_reads<A_KMAJOR, B_KMAJOR>();
+#pragma unroll
+  for (int s = 0; s < SUB; ++s) {
+    if (s + 1 < SUB) {
+      read_frags<A_KMAJOR, B_KMAJOR>(cur, s + 1, wm, wn, lane, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+      mfma_step(fa[s & 1], fb[s & 1], acc);
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 16 - NR, 0);
+    } else if constexpr (!LAST) {
+      stage_barrier<WAIT_OUT>();
+      read_frags<A_KMAJOR, B_KMAJOR>(nxt, 0, wm, wn, lane, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+      if constexpr (REFILL) dma(cur, refill_step);
+      mfma_step(fa[s & 1], fb[s & 1], acc);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NR, 0);
+      if constexpr (REFILL) {
+#pragma unroll
+        for (int i = 0; i < LOADS_PER_STAGE; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 16 - LOADS_PER_STAGE, 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 16, 0);
+      }
+    } else {
+      mfma_step(fa[s & 1], fb[s & 1], acc);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// The main loop over nk stages of BK; nk must be a multiple of NST (callers
+// pad K to NST * BK with operands that are zero there).  acc[mb][nb] is the
+// 32x32 block at rows wm*128 + 32*mb, columns wn*128 + 32*nb of the tile.
+template <bool A_KMAJOR, bool B_KMAJOR>
+__device__ __forceinline__ void mainloop(const Operand& A, const Operand& B, int m0, int n0, int nk, bf16* s0,
+                                         bf16* s1, bf16* s2, bf16* s3, f32x16 (&acc)[4][4]) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -145,41 +290,40 @@ __device__ __forceinline__ void mainloop(const Operand& A, const Operand& B, int
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  if (nk <= 0) return;
 
-  auto stage_load = [&](int stage, int k0) {
-    bf16* sa = smem + stage * STAGE_ELEMS;
-    bf16* sb = sa + TILE_ELEMS;
-    if constexpr (A_KMAJOR) load_tile_kmajor(A, m0, k0, sa, wave, lane);
-    else load_tile_mnmajor(A, m0, k0, sa, wave, lane);
-    if constexpr (B_KMAJOR) load_tile_kmajor(B, n0, k0, sb, wave, lane);
-    else load_tile_mnmajor(B, n0, k0, sb, wave, lane);
+  const Loader<A_KMAJOR> la(A, m0, wave, lane);
+  const Loader<B_KMAJOR> lb(B, n0, wave, lane);
+  auto dma = [&](bf16* stage, int step) {
+    la.issue(stage, step * BK, wave);
+    lb.issue(stage + TILE_ELEMS, step * BK, wave);
   };
+  constexpr int L = LOADS_PER_STAGE;
 
-  if (k_steps > 0) stage_load(0, 0);
-  for (int it = 0; it < k_steps; ++it) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (it + 1 < k_steps) stage_load((it + 1) & 1, (it + 1) * BK);
-    const bf16* sa = smem + (it & 1) * STAGE_ELEMS;
-    const bf16* sb = sa + TILE_ELEMS;
-#pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      bf16x8 fa[4], fb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if constexpr (A_KMAJOR) fa[i] = frag_kmajor(sa, wm * 128 + 32 * i + (lane & 31), s, lane);
-        else fa[i] = frag_mnmajor(sa, wm * 128 + 32 * i, s, lane);
-        if constexpr (B_KMAJOR) fb[i] = frag_kmajor(sb, wn * 128 + 32 * i + (lane & 31), s, lane);
-        else fb[i] = frag_mnmajor(sb, wn * 128 + 32 * i, s, lane);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
+  // Prologue: stages 0..3 in flight, then wait for stage 0.
+  dma(s0, 0);
+  dma(s1, 1);
+  dma(s2, 2);
+  dma(s3, 3);
+  stage_barrier<3 * L>();
+  bf16x8 fa[2][4], fb[2][4];
+  read_frags<A_KMAJOR, B_KMAJOR>(s0, 0, wm, wn, lane, fa[0], fb[0]);
+
+  // Steady state: each stage hands over to the next with two stages still
+  // in flight and refills itself NST steps ahead.
+  int it = 0;
+  for (; it + NST < nk; it += NST) {
+    stage_compute<A_KMAJOR, B_KMAJOR, 2 * L, true, false>(s0, s1, it + 4, dma, wm, wn, lane, fa, fb, acc);
+    stage_compute<A_KMAJOR, B_KMAJOR, 2 * L, true, false>(s1, s2, it + 5, dma, wm, wn, lane, fa, fb, acc);
+    stage_compute<A_KMAJOR, B_KMAJOR, 2 * L, true, false>(s2, s3, it + 6, dma, wm, wn, lane, fa, fb, acc);
+    stage_compute<A_KMAJOR, B_KMAJOR, 2 * L, true, false>(s3, s0, it + 7, dma, wm, wn, lane, fa, fb, acc);
   }
-  __syncthreads();
+  // Last four stages: nothing left to issue, the in-flight count drains.
+  stage_compute<A_KMAJOR, B_KMAJOR, 2 * L, false, false>(s0, s1, 0, dma, wm, wn, lane, fa, fb, acc);
+  stage_compute<A_KMAJOR, B_KMAJOR, L, false, false>(s1, s2, 0, dma, wm, wn, lane, fa, fb, acc);
+  stage_compute<A_KMAJOR, B_KMAJOR, 0, false, false>(s2, s3, 0, dma, wm, wn, lane, fa, fb, acc);
+  stage_compute<A_KMAJOR, B_KMAJOR, 0, false, true>(s3, s0, 0, dma, wm, wn, lane, fa, fb, acc);
+  stage_barrier<0>();
 }
 
 // Row / column of accumulator register r of block (mb, nb) within the tile.
@@ -189,11 +333,14 @@ __device__ __forceinline__ int acc_row(int wm, int mb, int r, int lane) {
 __device__ __forceinline__ int acc_col(int wn, int nb, int lane) { return wn * 128 + 32 * nb + (lane & 31); }
 
 // The kernel: schedule, early exit for tiles past the valid tokens, main loop,
-// then the epilogue.
+// then the epilogue (which may reuse the first stage's LDS).
 template <bool A_KMAJOR, bool B_KMAJOR, class Epi>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(Operand A, Operand B, Schedule sch,
                                                             typename Epi::Params ep) {
-  __shared__ __attribute__((aligned(1024))) bf16 smem[SMEM_ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 s0[STAGE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 s1[STAGE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 s2[STAGE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 s3[STAGE_ELEMS];
   int tm, tn;
   tile_of(blockIdx.x, sch.tiles_m, sch.tiles_n, tm, tn);
   const int m0 = tm * BM;
@@ -203,11 +350,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(Operand A, Operand B,
     const int tv = *sch.tok_count;
     if (sch.tok_dim == 1 && m0 >= tv) return;
     if (sch.tok_dim == 2 && n0 >= tv) return;
-    if (sch.tok_dim == 3) k_steps = (tv + BK - 1) / BK;
+    if (sch.tok_dim == 3) k_steps = (tv + NST * BK - 1) / (NST * BK) * NST;
   }
   f32x16 acc[4][4];
-  mainloop<A_KMAJOR, B_KMAJOR>(A, B, m0, n0, k_steps, smem, acc);
-  Epi::apply(ep, acc, m0, n0, smem);
+  mainloop<A_KMAJOR, B_KMAJOR>(A, B, m0, n0, k_steps, s0, s1, s2, s3, acc);
+  Epi::apply(ep, acc, m0, n0, s0);
 }
 
 }  // namespace gemm

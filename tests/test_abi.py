@@ -76,6 +76,7 @@ def test_workspace_size_bounds():
     (dict(reduction=2), _lib.FLCE_ERR_INVALID_ARG),
     (dict(num_label_tokens=0), _lib.FLCE_ERR_INVALID_ARG),
     (dict(hidden=100), _lib.FLCE_ERR_UNSUPPORTED),
+    (dict(hidden=192), _lib.FLCE_ERR_UNSUPPORTED),
     (dict(weight_dtype=1), _lib.FLCE_ERR_UNSUPPORTED),
 ])
 def test_invalid_problem_rejected(kw, expect):

@@ -29,11 +29,11 @@ def _small(key, **kw):
 
 SMALL = {
     "tiny": WORKLOADS[1],
-    "ragged_softcap_mean_pad": _small(101, T=600, H=320, V=1300, Vu=1100, w_std=0.3, pad_std=30.0,
+    "ragged_softcap_mean_pad": _small(101, T=600, H=384, V=1300, Vu=1100, w_std=0.3, pad_std=30.0,
                                       softcap=7.0, reduction="mean", ignore_frac=0.1),
     "multichunk_sum_runs": _small(102, T=1000, H=512, V=3000, Vu=3000, w_std=2.0 / math.sqrt(512),
                                   ignore="runs"),
-    "count_normalised": _small(103, T=777, H=192, V=2100, Vu=2049, w_std=0.1, softcap=30.0,
+    "count_normalised": _small(103, T=777, H=256, V=2100, Vu=2049, w_std=0.1, softcap=30.0,
                                ignore_frac=0.3, normalise_by_count=True),
     "peaked": _small(104, T=300, H=256, V=4099, Vu=4099, w_std=0.4, softcap=30.0, ignore_frac=0.02,
                      labels="argmax70"),
