@@ -10,7 +10,7 @@
 // 16 KB each), each its own __shared__ array.  Stages are filled by
 // global_load_lds_dwordx4, which writes each lane's 16 bytes straight into
 // LDS (no VGPR staging, no LDS write instructions), three stages ahead of the
-// stage being multiplied.  Separate arrays let the compiler see that a DMA in
+// stage being multiplied and spread across a stage's MFMAs.  Separate arrays let the compiler see that a DMA in
 // flight never aliases the stage being read, so it does not stall LDS reads
 // on it; the wait before each workgroup barrier names how many DMA
 // instructions may still be outstanding.
@@ -25,14 +25,12 @@
 // global layout, so global loads stay fully coalesced either way:
 //  - K-major tile: 256 rows x 32 k (64-byte rows).  A fragment (one row,
 //    8 consecutive k) is one ds_read_b128.  The 16-byte chunk c of row r sits
-//    at chunk c ^ swz_k(r), so the lanes the LDS services together (16 per
-//    cycle with 64 banks, 8 with 32) hit distinct banks.
+//    at chunk c ^ swz_k(r), which leaves these reads free of bank conflicts.
 //  - MN-major tile: 32 k-rows x 256 mn (512-byte rows).  A fragment is two
 //    ds_read_b64_tr_b16: within each 16-lane group the hardware transposes a
 //    4 (k) x 16 (mn) block so that lane i receives column i, four
-//    consecutive k.  Pairs of 16-byte chunks are XOR-swizzled per k-row so
-//    the four rows a group reads, and the two groups of a half-wave, hit
-//    distinct banks.
+//    consecutive k.  Pairs of 16-byte chunks are XOR-swizzled per k-row,
+//    which leaves these reads free of bank conflicts.
 //
 // The accumulator layout of the 32x32 MFMA: lane l, register r holds element
 // (row 8*(r/4) + 4*(l/32) + r%4, column l%32) of its block.
@@ -70,14 +68,25 @@ struct Schedule {
   int tok_dim;              // 0: none, 1: M is tokens, 2: N is tokens, 3: K is tokens
 };
 
-__device__ __forceinline__ int swz_k(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// Chosen by measurement (SQ_LDS_BANK_CONFLICT on gfx950 for this exact
+// read pattern): XOR-ing chunks with bits 2..3 of the row leaves the
+// ds_read_b128 of both k steps conflict-free.
+__device__ __forceinline__ int swz_k(int r) { return (r >> 2) & 3; }
 
 // Chunk XOR for MN-major rows: pairs of 16-byte chunks are XOR-ed with
 // t(k % 4) in {0, 3, 5, 6}; t and t ^ 1 cover all eight pair slots of 256 B.
 __device__ __forceinline__ int swz_mn(int k) { return ((0x6530 >> ((k & 3) * 4)) & 0xF) << 1; }
 
-__device__ __forceinline__ void lds_dma16(const bf16* src, bf16* lds_dst) {
-  __builtin_amdgcn_global_load_lds((const void*)src, (FLCE_LDS void*)lds_dst, 16, 0, 0);
+// Global -> LDS copy of 16 bytes per lane through a buffer resource: the
+// base address is uniform (SGPRs) and each lane supplies a 32-bit byte
+// offset, which costs the address unit half of what 64-bit per-lane
+// addresses do.  The LDS destination is wave-uniform; lane i's 16 bytes land
+// at lds_dst + 16 * i.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFF0, 0x00020000);
+}
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, unsigned voff, unsigned soff, bf16* lds_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FLCE_LDS void*)lds_dst, 16, voff, soff, 0, 0);
 }
 
 // s_waitcnt with vmcnt <= n (n < 64) and lgkmcnt = 0 (gfx9 encoding).
@@ -98,61 +107,74 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Per-thread DMA sources for one operand: a uniform base and per-lane
-// offsets that do not change along K (a K tail is clamped separately).
+// Per-thread DMA sources for one operand, fixed along K: the byte offset of
+// each of this thread's 16-byte pieces relative to the tile's origin.
+//  - K-major: resource based at the tile's first row; stage k0 adds 2*k0
+//    bytes through the scalar offset.
+//  - MN-major: resource rebased at k-row k0 for every stage (scalar work);
+//    rows past k_max read as zero (the partner operand is zero there too).
 template <bool KMAJOR>
 struct Loader {
-  const bf16* base;        // uniform
+  const bf16* base;
   int64_t ld;
   int k_max;
-  int off[LOADS_PER_TILE]; // elements from base (+ k0 or k0*ld)
-  int kk[LOADS_PER_TILE];  // MN-major: k row within the stage
-  int col[LOADS_PER_TILE]; // MN-major: column offset within the row
+  __amdgpu_buffer_rsrc_t rsrc;      // K-major only
+  unsigned off[LOADS_PER_TILE];     // bytes
+  int kk[LOADS_PER_TILE];           // MN-major: k row within the stage
+  int col[LOADS_PER_TILE];          // MN-major: column (elements)
 
   __device__ __forceinline__ Loader(const Operand& op, int mn0, int wave, int lane) {
     ld = op.ld;
     k_max = op.k_max;
     if constexpr (KMAJOR) {
       base = op.ptr + (int64_t)mn0 * op.ld;
+      rsrc = make_rsrc(base);
 #pragma unroll
       for (int q = 0; q < LOADS_PER_TILE; ++q) {
         const int b = wave * LOADS_PER_TILE + q;   // 1 KB block: 16 rows of 64 B
         const int r = b * 16 + (lane >> 2);
         const int c = (lane & 3) ^ swz_k(r);
         const int gr = min(mn0 + r, op.mn_max) - mn0;
-        off[q] = gr * (int)op.ld + c * 8;
+        off[q] = (unsigned)(gr * (int)op.ld + c * 8) * 2u;
         kk[q] = 0;
         col[q] = 0;
       }
     } else {
       base = op.ptr;
+      rsrc = make_rsrc(base);
 #pragma unroll
       for (int q = 0; q < LOADS_PER_TILE; ++q) {
         const int b = wave * LOADS_PER_TILE + q;   // 1 KB block: 2 k-rows of 512 B
         kk[q] = b * 2 + (lane >> 5);
         const int c = (lane & 31) ^ swz_mn(kk[q]);
         col[q] = min(mn0 + c * 8, op.mn_max - 7);
-        off[q] = kk[q] * (int)op.ld + col[q];
+        off[q] = (unsigned)(kk[q] * (int)op.ld + col[q]) * 2u;
       }
     }
   }
 
   // Issue this thread's share of the stage starting at k0 into `tile`.
-  // MN-major rows past k_max are clamped to it (their partner operand is
-  // zero there); K-major operands are read in full rows of padded K.
   __device__ __forceinline__ void issue(bf16* tile, int k0, int wave) const {
     if constexpr (KMAJOR) {
-      const bf16* src = base + k0;
+      const unsigned soff = (unsigned)k0 * 2u;
 #pragma unroll
       for (int q = 0; q < LOADS_PER_TILE; ++q)
-        lds_dma16(src + off[q], tile + (wave * LOADS_PER_TILE + q) * 512);
+        lds_dma16(rsrc, off[q], soff, tile + (wave * LOADS_PER_TILE + q) * 512);
     } else {
-      const bf16* src = base + (int64_t)k0 * ld;
-      const int krem = k_max - k0;
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (int64_t)k0 * ld);
+      if (k0 + BK - 1 <= k_max) {
 #pragma unroll
-      for (int q = 0; q < LOADS_PER_TILE; ++q) {
-        const int kr = min(kk[q], krem);
-        lds_dma16(src + (kr * (int)ld + col[q]), tile + (wave * LOADS_PER_TILE + q) * 512);
+        for (int q = 0; q < LOADS_PER_TILE; ++q)
+          lds_dma16(r, off[q], 0, tile + (wave * LOADS_PER_TILE + q) * 512);
+      } else {
+        // Rows past k_max read as zero: their offsets are made out of range,
+        // which the buffer unit answers with zeros and no memory access.
+        const int krem = k_max - k0;
+#pragma unroll
+        for (int q = 0; q < LOADS_PER_TILE; ++q) {
+          const unsigned o = kk[q] <= krem ? off[q] : 0x80000000u;
+          lds_dma16(r, o, 0, tile + (wave * LOADS_PER_TILE + q) * 512);
+        }
       }
     }
   }
@@ -204,16 +226,24 @@ __device__ __forceinline__ void mfma_step(const bf16x8 (&fa)[4], const bf16x8 (&
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
 }
 
-// Map a workgroup id to a tile so that the workgroups one XCD runs (ids that
-// are equal mod 8) get a contiguous run of tiles, with N varying fastest.
+// Map a workgroup id to a tile.  The hardware deals workgroup ids to the 8
+// XCDs round-robin, so ids equal mod 8 share an XCD (and its L2): each XCD
+// gets a contiguous run of tiles, and within the run tiles go in groups of
+// 8 M-tiles per N-tile column, so the 32 workgroups an XCD runs at once
+// cover about 8 x 4 tiles and share both operands' k-slabs in L2.
+constexpr int GROUP_M = 8;
 __device__ __forceinline__ void tile_of(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int total = tiles_m * tiles_n;
   const int xcd = pid & 7;
   const int local = pid >> 3;
-  const int base = xcd * (total >> 3) + min(xcd, total & 7);
-  const int logical = base + local;
-  tm = logical / tiles_n;
-  tn = logical - tm * tiles_n;
+  const int l = xcd * (total >> 3) + min(xcd, total & 7) + local;
+  const int per_group = GROUP_M * tiles_n;
+  const int gid = l / per_group;
+  const int first_m = gid * GROUP_M;
+  const int gsz = min(tiles_m - first_m, GROUP_M);
+  const int r = l - gid * per_group;
+  tm = first_m + r % gsz;
+  tn = r / gsz;
 }
 
 // LDS read instructions one read_frags issues.
@@ -226,57 +256,88 @@ constexpr int kSchedVmemRead = 0x020;
 constexpr int kSchedDsRead = 0x100;
 
 // One stage of the main loop: the MFMA k steps of stage `cur`, with the
-// hand-over to stage `nxt` before the last step.  WAIT_OUT is the number of
-// this thread's DMA instructions that may still be in flight at the barrier
-// (the stages issued after `nxt`); REFILL issues stage `refill_step` into
-// `cur` once every wave is done reading it; LAST skips the hand-over.
-//
-// Instruction order is pinned per k step: the next step's LDS reads are
-// spread between this step's 16 MFMAs, so their latency hides behind the
-// MFMAs instead of stalling them.  After the hand-over barrier the next
-// stage's first reads go out first, then the refill DMAs between MFMAs.
-template <bool A_KMAJOR, bool B_KMAJOR, int WAIT_OUT, bool REFILL, bool LAST, class DMA>
-__device__ __forceinline__ void stage_compute(bf16* cur, bf16* nxt, int refill_step, const DMA& dma, int wm, int wn,
-                                              int lane, bf16x8 (&fa)[2][4], bf16x8 (&fb)[2][4],
-                                              f32x16 (&acc)[4][4]) {
+// hand-over to stage `nxt` before the last step.
+//  - REFILL: issue stage `refill_step` into `refill`, the buffer every wave
+//    finished reading before the previous hand-over barrier: the A half
+//    during the first k step, the B half during the second.
+//  - WAIT_OUT: this thread's DMA instructions that may still be in flight at
+//    the hand-over barrier (those issued after stage `nxt`'s).
+//  - LAST: no hand-over.
+// Instruction order is pinned per k step: the next step's LDS reads and the
+// refill DMAs are spread evenly between the step's 16 MFMAs.  A DMA issue
+// can stall the wave while the address unit is busy, and a stalled wave
+// issues no MFMA, so no two DMAs sit next to each other.  After the
+// hand-over barrier the next stage's first reads go out first.
+template <int NR, int NV>
+__device__ __forceinline__ void interleave_step() {
+  // 16 MFMAs; NR LDS reads and NV DMAs distributed across them.
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if (i < NR) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    if (NV > 0 && (i % (16 / (NV > 0 ? NV : 1))) == 0 && i / (16 / (NV > 0 ? NV : 1)) < NV)
+      __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+  }
+}
+
+#ifndef FLCE_SPREAD_REFILL
+#define FLCE_SPREAD_REFILL 1
+#endif
+// Refill placement: 0 = all of a stage's DMAs in its first k step, 1 = the A
+// half in the first, the B half in the second.
+constexpr bool kSpreadRefill = FLCE_SPREAD_REFILL != 0;
+// DMA instructions of the refill still outstanding at a hand-over barrier
+// beyond the next-but-one stage.
+constexpr int kRefillOutAtBarrier = kSpreadRefill ? LOADS_PER_TILE : LOADS_PER_STAGE;
+
+template <bool A_KMAJOR, bool B_KMAJOR, int WAIT_OUT, bool REFILL, bool LAST, class LA, class LB>
+__device__ __forceinline__ void stage_compute(bf16* cur, bf16* nxt, bf16* refill, int refill_step, const LA& la,
+                                              const LB& lb, int wave, int wm, int wn, int lane, bf16x8 (&fa)[2][4],
+                                              bf16x8 (&fb)[2][4], f32x16 (&acc)[4][4]) {
   constexpr int NR = frag_reads<A_KMAJOR, B_KMAJOR>();
+  constexpr int NV0 = REFILL ? (kSpreadRefill ? LOADS_PER_TILE : LOADS_PER_STAGE) : 0;
+  constexpr int NV1 = REFILL && kSpreadRefill ? LOADS_PER_TILE : 0;
+  static_assert(SUB == 2, "two k steps per stage");
+  // k step 0: next step's fragments, (part of) the refill, 16 MFMAs.
+  read_frags<A_KMAJOR, B_KMAJOR>(cur, 1, wm, wn, lane, fa[1], fb[1]);
+  if constexpr (REFILL) {
+    la.issue(refill, refill_step * BK, wave);
+    if constexpr (!kSpreadRefill) lb.issue(refill + TILE_ELEMS, refill_step * BK, wave);
+  }
+  mfma_step(fa[0], fb[0], acc);
+  interleave_step<NR, NV0>();
+  __builtin_amdgcn_sched_barrier(0);
+  // k step 1: hand over to the next stage, (the rest of) the refill, then
+  // the last 16 MFMAs.
+  if constexpr (!LAST) {
+    stage_barrier<WAIT_OUT>();
+    read_frags<A_KMAJOR, B_KMAJOR>(nxt, 0, wm, wn, lane, fa[0], fb[0]);
+    if constexpr (NV1 > 0) lb.issue(refill + TILE_ELEMS, refill_step * BK, wave);
+    mfma_step(fa[1], fb[1], acc);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NR, 0);
+    if constexpr (NV1 > 0) {
 #pragma unroll
-  for (int s = 0; s < SUB; ++s) {
-    if (s + 1 < SUB) {
-      read_frags<A_KMAJOR, B_KMAJOR>(cur, s + 1, wm, wn, lane, fa[(s + 1) & 1], fb[(s + 1) & 1]);
-      mfma_step(fa[s & 1], fb[s & 1], acc);
-#pragma unroll
-      for (int i = 0; i < NR; ++i) {
+      for (int i = 0; i < 16; ++i) {
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 16 - NR, 0);
-    } else if constexpr (!LAST) {
-      stage_barrier<WAIT_OUT>();
-      read_frags<A_KMAJOR, B_KMAJOR>(nxt, 0, wm, wn, lane, fa[(s + 1) & 1], fb[(s + 1) & 1]);
-      if constexpr (REFILL) dma(cur, refill_step);
-      mfma_step(fa[s & 1], fb[s & 1], acc);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NR, 0);
-      if constexpr (REFILL) {
-#pragma unroll
-        for (int i = 0; i < LOADS_PER_STAGE; ++i) {
-          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 16 - LOADS_PER_STAGE, 0);
-      } else {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 16, 0);
+        if ((i & 3) == 0) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
       }
     } else {
-      mfma_step(fa[s & 1], fb[s & 1], acc);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 16, 0);
     }
-    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    mfma_step(fa[1], fb[1], acc);
   }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // The main loop over nk stages of BK; nk must be a multiple of NST (callers
 // pad K to NST * BK with operands that are zero there).  acc[mb][nb] is the
 // 32x32 block at rows wm*128 + 32*mb, columns wn*128 + 32*nb of the tile.
+//
+// Stage j lives in buffer j % 4.  Stages 0..2 are issued up front; stage
+// it+3 is issued during stage it into the buffer of stage it-1, so three
+// stages are always in flight or resident and a DMA has about two stages of
+// MFMA time to land.
 template <bool A_KMAJOR, bool B_KMAJOR>
 __device__ __forceinline__ void mainloop(const Operand& A, const Operand& B, int m0, int n0, int nk, bf16* s0,
                                          bf16* s1, bf16* s2, bf16* s3, f32x16 (&acc)[4][4]) {
@@ -300,29 +361,28 @@ __device__ __forceinline__ void mainloop(const Operand& A, const Operand& B, int
   };
   constexpr int L = LOADS_PER_STAGE;
 
-  // Prologue: stages 0..3 in flight, then wait for stage 0.
+  // Prologue: stages 0..2 in flight, then wait for stage 0.
   dma(s0, 0);
   dma(s1, 1);
   dma(s2, 2);
-  dma(s3, 3);
-  stage_barrier<3 * L>();
+  stage_barrier<2 * L>();
   bf16x8 fa[2][4], fb[2][4];
   read_frags<A_KMAJOR, B_KMAJOR>(s0, 0, wm, wn, lane, fa[0], fb[0]);
 
-  // Steady state: each stage hands over to the next with two stages still
-  // in flight and refills itself NST steps ahead.
+  // At the hand-over barrier of stage it, stage it+1 must have landed; still
+  // in flight may be stage it+2 and what was issued of stage it+3.
   int it = 0;
   for (; it + NST < nk; it += NST) {
-    stage_compute<A_KMAJOR, B_KMAJOR, 2 * L, true, false>(s0, s1, it + 4, dma, wm, wn, lane, fa, fb, acc);
-    stage_compute<A_KMAJOR, B_KMAJOR, 2 * L, true, false>(s1, s2, it + 5, dma, wm, wn, lane, fa, fb, acc);
-    stage_compute<A_KMAJOR, B_KMAJOR, 2 * L, true, false>(s2, s3, it + 6, dma, wm, wn, lane, fa, fb, acc);
-    stage_compute<A_KMAJOR, B_KMAJOR, 2 * L, true, false>(s3, s0, it + 7, dma, wm, wn, lane, fa, fb, acc);
+    stage_compute<A_KMAJOR, B_KMAJOR, L + kRefillOutAtBarrier, true, false>(s0, s1, s3, it + 3, la, lb, wave, wm, wn, lane, fa, fb, acc);
+    stage_compute<A_KMAJOR, B_KMAJOR, L + kRefillOutAtBarrier, true, false>(s1, s2, s0, it + 4, la, lb, wave, wm, wn, lane, fa, fb, acc);
+    stage_compute<A_KMAJOR, B_KMAJOR, L + kRefillOutAtBarrier, true, false>(s2, s3, s1, it + 5, la, lb, wave, wm, wn, lane, fa, fb, acc);
+    stage_compute<A_KMAJOR, B_KMAJOR, L + kRefillOutAtBarrier, true, false>(s3, s0, s2, it + 6, la, lb, wave, wm, wn, lane, fa, fb, acc);
   }
-  // Last four stages: nothing left to issue, the in-flight count drains.
-  stage_compute<A_KMAJOR, B_KMAJOR, 2 * L, false, false>(s0, s1, 0, dma, wm, wn, lane, fa, fb, acc);
-  stage_compute<A_KMAJOR, B_KMAJOR, L, false, false>(s1, s2, 0, dma, wm, wn, lane, fa, fb, acc);
-  stage_compute<A_KMAJOR, B_KMAJOR, 0, false, false>(s2, s3, 0, dma, wm, wn, lane, fa, fb, acc);
-  stage_compute<A_KMAJOR, B_KMAJOR, 0, false, true>(s3, s0, 0, dma, wm, wn, lane, fa, fb, acc);
+  // Last four stages: one refill left, then the in-flight count drains.
+  stage_compute<A_KMAJOR, B_KMAJOR, L + kRefillOutAtBarrier, true, false>(s0, s1, s3, it + 3, la, lb, wave, wm, wn, lane, fa, fb, acc);
+  stage_compute<A_KMAJOR, B_KMAJOR, L, false, false>(s1, s2, s0, 0, la, lb, wave, wm, wn, lane, fa, fb, acc);
+  stage_compute<A_KMAJOR, B_KMAJOR, 0, false, false>(s2, s3, s1, 0, la, lb, wave, wm, wn, lane, fa, fb, acc);
+  stage_compute<A_KMAJOR, B_KMAJOR, 0, false, true>(s3, s0, s2, 0, la, lb, wave, wm, wn, lane, fa, fb, acc);
   stage_barrier<0>();
 }
 
