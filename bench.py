@@ -31,6 +31,18 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources; HBM byte counts measured on other sources are stale."""
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "lm_head_cross_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
 def cpu_baseline(inp, n_tokens):
     """Time the oracle (fwd + bwd, full vocabulary) on the first n_tokens
     positions of the workload; returns tokens/s and what was run."""
@@ -69,8 +81,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2)
-    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-tokens", type=int, default=3072)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="after timing, copy this many MiB once (a plain copy kernel of known size, "
+                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch of the dominant kernel, from rocprofv3 counters")
     args = ap.parse_args()
@@ -124,12 +139,14 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
     records = trace.records()
 
+    # The library prices a contraction launch at 2*T*rows*H; only the Tv
+    # valid tokens are work the method does, so rescale to 2*Tv*rows*H.
     kinds = {}
     for kind, kms, fl in records:
         k = kinds.setdefault(kind, {"launches": 0, "ms": 0.0, "flops": 0.0})
         k["launches"] += 1
         k["ms"] += kms
-        k["flops"] += fl
+        k["flops"] += fl * Tv / T
     for name, k in sorted(kinds.items(), key=lambda kv: -kv[1]["ms"]):
         tf = k["flops"] / (k["ms"] * 1e-3) / 1e12 if k["flops"] else 0.0
         log(f"  {name:12s} launches={k['launches']:5d} total={k['ms'] / args.steps:8.3f} ms/step "
@@ -141,7 +158,7 @@ def main():
         with open(args.traffic_json) as f:
             tj = json.load(f)
         entry = tj.get(f"workload{w.key}", {}).get(dom_name)
-        if entry and entry.get("source_hash") == tj.get("kernel_source_hash"):
+        if entry and tj.get("kernel_source_hash") == kernel_source_hash():
             traffic = entry.get("bytes_per_launch")
     roofline = {
         "kernel": dom_name,
@@ -159,6 +176,16 @@ def main():
     pct_peak = credited / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12) * 100.0
     log(f"step {ms:.3f} ms  {tokens_per_s:,.0f} tokens/s  {pct_peak:.1f}% of bf16 peak "
         f"(credited {credited / 1e12:.2f} TFLOP)  loss={loss.item():.6g}")
+
+    if args.calibration_copy_mib > 0:
+        n = args.calibration_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {n} bytes read, {n} bytes written")
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -189,6 +216,7 @@ def main():
             "label_tokens_per_s": round(Tv / (ms * 1e-3), 1),
         },
         "roofline": roofline,
+        "kernel_source_hash": kernel_source_hash(),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
