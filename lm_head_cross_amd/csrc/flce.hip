@@ -88,36 +88,51 @@ __global__ __launch_bounds__(256) void k_gather(const uint4* __restrict__ X, int
   }
 }
 
-// Per compacted token: merge the vocab-tile partials in tile order into the
-// log-sum-exp, form the token loss, and reduce the block's losses in fp64.
-__global__ __launch_bounds__(256) void k_combine(const float2* __restrict__ partials, int tiles_v, int ldp,
-                                                  const float* __restrict__ label_logit,
-                                                  const int32_t* __restrict__ valid_idx, const Meta* meta,
-                                                  float* lse_out, float* tl_out, double* block_sums) {
-  __shared__ double red[256];
+// Per compacted token: merge the vocab-tile partials into the log-sum-exp,
+// form the token loss, and reduce the block's losses in fp64.  A block takes
+// kCombineTokens consecutive tokens; its kCombineSlices thread rows each merge
+// every kCombineSlices-th tile (reads stay coalesced across the tokens), then
+// the slices are merged in slice order.  The order is fixed, so the result is
+// deterministic.
+constexpr int kCombineTokens = 64;
+constexpr int kCombineSlices = 16;
+__global__ __launch_bounds__(kCombineTokens * kCombineSlices) void k_combine(
+    const float2* __restrict__ partials, int tiles_v, int ldp, const float* __restrict__ label_logit,
+    const int32_t* __restrict__ valid_idx, const Meta* meta, float* lse_out, float* tl_out, double* block_sums) {
+  __shared__ float2 red[kCombineSlices][kCombineTokens];
+  __shared__ double lred[kCombineTokens];
   const int tv = meta->n_valid;
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  double loss = 0.0;
+  const int tok = threadIdx.x % kCombineTokens;
+  const int slice = threadIdx.x / kCombineTokens;
+  const int t = blockIdx.x * kCombineTokens + tok;
+  float m = kNegInf, s = 0.0f;
   if (t < tv) {
-    float m = kNegInf, s = 0.0f;
-    for (int j = 0; j < tiles_v; ++j) {
+    for (int j = slice; j < tiles_v; j += kCombineSlices) {
       const float2 pr = partials[(int64_t)j * ldp + t];
       lse_merge(m, s, pr.x, pr.y);
     }
-    const float lse = m + log_e(s);
-    const float l = lse - label_logit[t];
-    const int orig = valid_idx[t];
-    lse_out[orig] = lse;
-    if (tl_out) tl_out[orig] = l;
-    loss = (double)l;
   }
-  red[threadIdx.x] = loss;
+  red[slice][tok] = make_float2(m, s);
   __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
-    __syncthreads();
+  if (slice == 0) {
+    for (int k = 1; k < kCombineSlices; ++k) lse_merge(m, s, red[k][tok].x, red[k][tok].y);
+    double loss = 0.0;
+    if (t < tv) {
+      const float lse = m + log_e(s);
+      const float l = lse - label_logit[t];
+      const int orig = valid_idx[t];
+      lse_out[orig] = lse;
+      if (tl_out) tl_out[orig] = l;
+      loss = (double)l;
+    }
+    lred[tok] = loss;
   }
-  if (threadIdx.x == 0) block_sums[blockIdx.x] = red[0];
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double acc = 0.0;
+    for (int k = 0; k < kCombineTokens; ++k) acc += lred[k];
+    block_sums[blockIdx.x] = acc;
+  }
 }
 
 // Normaliser D: num_label_tokens when given, else Tv for MEAN, else 1.
@@ -241,7 +256,7 @@ Plan make_plan(const flce_problem_t* p) {
   pl.off_yc = take(pl.Tvp * 4);
   pl.off_label = take(pl.Tvp * 4);
   pl.off_scale = take(16);
-  pl.off_bsum = take(pl.tiles_t * 8);
+  pl.off_bsum = take(pl.Tvp / kCombineTokens * 8);
   pl.off_xc = take(pl.Tvp * pl.H * 2);
   const size_t common = o;
   pl.off_part = take(pl.tiles_v * pl.Tvp * 8);
@@ -436,13 +451,15 @@ int flce_forward(const flce_problem_t* problem, const void* hidden, const void* 
   }
   {
     TraceScope tr(FLCE_KERNEL_COMBINE, 0.0, stream);
-    hipLaunchKernelGGL(k_combine, dim3(pl.tiles_t), dim3(256), 0, stream, (const float2*)part, (int)pl.tiles_v,
+    hipLaunchKernelGGL(k_combine, dim3(pl.Tvp / kCombineTokens), dim3(kCombineTokens * kCombineSlices), 0, stream,
+                       (const float2*)part, (int)pl.tiles_v,
                        (int)pl.Tvp, (const float*)label_logit, (const int32_t*)valid_idx, (const Meta*)meta, lse,
                        token_loss, bsum);
   }
   {
     TraceScope tr(FLCE_KERNEL_FINALIZE, 0.0, stream);
-    hipLaunchKernelGGL(k_finalize, dim3(1), dim3(256), 0, stream, (const double*)bsum, (int)pl.tiles_t,
+    hipLaunchKernelGGL(k_finalize, dim3(1), dim3(256), 0, stream, (const double*)bsum,
+                       (int)(pl.Tvp / kCombineTokens),
                        (const Meta*)meta, (int)p.reduction, p.num_label_tokens, loss);
   }
   return launch_status();
