@@ -233,7 +233,50 @@ int validate(const flce_problem_t* p) {
   return FLCE_OK;
 }
 
-Plan make_plan(const flce_problem_t* p) {
+// Width, in 256-row vocabulary tiles, of the backward pass's chunks.  A chunk
+// of ct tiles launches tiles_t * ct recompute tiles (depth H) and ct * tiles_h
+// dW tiles (depth Tvp); a launch of n tiles runs in about ceil(n / CUs)
+// rounds, one tile per CU per round.  The dH contraction's cost does not
+// depend on the split, apart from its fp32 accumulator pass, which is counted
+// with the launch overhead as a fixed cost per chunk.  Among widths up to
+// ct_max this picks the one with the least estimated time (ties: the wider).
+constexpr int64_t kChunkOverheadDepth = 1536;  // per chunk, in units of one round's depth
+int64_t pick_chunk_tiles(int64_t tiles_v, int64_t tiles_t, int64_t tiles_h, int64_t H, int64_t Tvp, int64_t ct_max,
+                         int n_cu) {
+  auto cost = [&](int64_t ct) {
+    const int64_t full = tiles_v / ct;
+    const int64_t rem = tiles_v - full * ct;
+    auto chunk = [&](int64_t c) {
+      return ceil_div(tiles_t * c, n_cu) * H + ceil_div(c * tiles_h, n_cu) * Tvp + kChunkOverheadDepth;
+    };
+    return full * chunk(ct) + (rem ? chunk(rem) : 0);
+  };
+  int64_t best = ct_max;
+  int64_t best_cost = cost(ct_max);
+  for (int64_t ct = ct_max - 1; ct >= 1; --ct) {
+    const int64_t c = cost(ct);
+    if (c < best_cost) {
+      best = ct;
+      best_cost = c;
+    }
+  }
+  return best;
+}
+
+// Compute units of the current device (256 on MI355X when the query fails).
+int device_cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+Plan make_plan(const flce_problem_t* p, int n_cu = 256) {
   Plan pl{};
   pl.T = p->num_tokens;
   pl.H = p->hidden;
@@ -244,10 +287,13 @@ Plan make_plan(const flce_problem_t* p) {
   pl.tiles_v = ceil_div(pl.Vu, 256);
   pl.tiles_h = ceil_div(pl.H, 256);
   // Chunk width: at most a quarter of the usable vocabulary (whole tiles), at
-  // least one tile; chunks of equal width up to the last.
-  const int64_t vc_max = std::max<int64_t>(256, (pl.Vu / 1024) * 256);
-  pl.nchunks = ceil_div(pl.Vu, vc_max);
-  pl.vc = align_up((size_t)ceil_div(pl.Vu, pl.nchunks), 256);
+  // least one tile; chunks of equal width up to the last.  The G buffer is
+  // sized for the widest chunk, so the workspace does not depend on the
+  // device.
+  const int64_t ct_max = std::max<int64_t>(1, pl.Vu / 1024);
+  const int64_t ct = pick_chunk_tiles(pl.tiles_v, pl.tiles_t, pl.tiles_h, pl.H, pl.Tvp, ct_max, n_cu);
+  pl.vc = ct * 256;
+  pl.nchunks = ceil_div(pl.tiles_v, ct);
 
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, kAlign); return at; };
@@ -262,8 +308,9 @@ Plan make_plan(const flce_problem_t* p) {
   pl.off_part = take(pl.tiles_v * pl.Tvp * 8);
   const size_t fwd_end = o;
   o = common;
-  pl.off_g = take(pl.Tvp * pl.vc * 2);
-  pl.off_hacc = take(pl.nchunks > 1 ? pl.Tvp * pl.H * 4 : 0);
+  pl.off_g = take(pl.Tvp * ct_max * 256 * 2);
+  // Every chunk width below tiles_v gives more than one chunk.
+  pl.off_hacc = take(pl.tiles_v > 1 ? pl.Tvp * pl.H * 4 : 0);
   const size_t bwd_end = o;
   pl.total = std::max(fwd_end, bwd_end);
   return pl;
@@ -480,7 +527,7 @@ int flce_backward(const flce_problem_t* problem, const void* hidden, const void*
     zero_fill(d_weight, p.vocab * p.hidden * 4, stream);
     return launch_status();
   }
-  const Plan pl = make_plan(&p);
+  const Plan pl = make_plan(&p, device_cu_count());
   if ((st = check_workspace(pl, workspace, workspace_bytes)) != FLCE_OK) return st;
 
   Meta* meta = ws_at<Meta>(workspace, pl.off_meta);
