@@ -8,17 +8,18 @@
 //
 // K advances 32 at a time through four LDS stages of 32 KB (A and B tiles of
 // 16 KB each), each its own __shared__ array.  Stages are filled by
-// global_load_lds_dwordx4, which writes each lane's 16 bytes straight into
-// LDS (no VGPR staging, no LDS write instructions), three stages ahead of the
-// stage being multiplied and spread across a stage's MFMAs.  Separate arrays let the compiler see that a DMA in
-// flight never aliases the stage being read, so it does not stall LDS reads
-// on it; the wait before each workgroup barrier names how many DMA
-// instructions may still be outstanding.
+// buffer_load_dwordx4 ... lds, which writes each lane's 16 bytes straight
+// into LDS (no VGPR staging, no LDS write instructions), three stages ahead
+// of the stage being multiplied and spread across a stage's MFMAs.  Separate
+// arrays let the compiler see that a DMA in flight never aliases the stage
+// being read, so it does not stall LDS reads on it; the wait before each
+// workgroup barrier names how many DMA instructions may still be
+// outstanding.
 //
-// Within a stage, the MFMA fragments of the next 16-wide k step are read
-// while the current step's 16 MFMAs issue.  The barrier that hands the next
-// stage over sits before the last k step's MFMAs, so those MFMAs cover the
-// barrier and the first LDS reads of the next stage.
+// The MFMA fragments of the next stage (both 16-wide k steps) are read while
+// the current stage's 32 MFMAs issue, into four register sets that rotate
+// every two stages.  One barrier per stage, at its start, hands the next
+// stage over.
 //
 // Either operand may be K-major (element (mn, k) at ptr[mn*ld + k]) or
 // MN-major (element (mn, k) at ptr[k*ld + mn]); the LDS tile keeps the
@@ -194,8 +195,16 @@ __device__ __forceinline__ bf16x8 frag_mnmajor(const bf16* tile, int col0, int s
   const int col = col0 + 16 * (g & 1) + 4 * (j & 3);
   const int k0 = 16 * s + 8 * (g >> 1) + (j >> 2);
   const int k1 = k0 + 4;
-  const bf16* p0 = tile + k0 * 256 + (((col >> 3) ^ swz_mn(k0)) << 3) + (col & 7);
-  const bf16* p1 = tile + k1 * 256 + (((col >> 3) ^ swz_mn(k1)) << 3) + (col & 7);
+  const int i0 = k0 * 256 + (((col >> 3) ^ swz_mn(k0)) << 3) + (col & 7);
+  int i1 = k1 * 256 + (((col >> 3) ^ swz_mn(k1)) << 3) + (col & 7);
+  // i1 is i0 + 1024; left visible, the optimizer splits that constant into a
+  // GEP of its own, one level too deep for the LDS lowering to attach the
+  // per-array alias scope, and the waitcnt pass then makes this read wait
+  // for every DMA in flight (vmcnt(0) each stage).  The empty asm keeps both
+  // addresses one GEP away from the tile.
+  asm("" : "+v"(i1));
+  const bf16* p0 = tile + i0;
+  const bf16* p1 = tile + i1;
   const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((FLCE_LDS bf16x4*)p0);
   const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((FLCE_LDS bf16x4*)p1);
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -255,22 +264,34 @@ constexpr int kSchedMfma = 0x008;
 constexpr int kSchedVmemRead = 0x020;
 constexpr int kSchedDsRead = 0x100;
 
-// One stage of the main loop: the MFMA k steps of stage `cur`, with the
-// hand-over to stage `nxt` before the last step.
-//  - REFILL: issue stage `refill_step` into `refill`, the buffer every wave
-//    finished reading before the previous hand-over barrier: the A half
-//    during the first k step, the B half during the second.
-//  - WAIT_OUT: this thread's DMA instructions that may still be in flight at
-//    the hand-over barrier (those issued after stage `nxt`'s).
-//  - LAST: no hand-over.
-// Instruction order is pinned per k step: the next step's LDS reads and the
-// refill DMAs are spread evenly between the step's 16 MFMAs.  A DMA issue
-// can stall the wave while the address unit is busy, and a stalled wave
-// issues no MFMA, so no two DMAs sit next to each other.  After the
-// hand-over barrier the next stage's first reads go out first.
+// s_waitcnt vmcnt <= VM, lgkmcnt <= LG, then the workgroup barrier.
+template <int VM, int LG>
+__device__ __forceinline__ void stage_barrier_lg() {
+  static_assert(VM >= 0 && VM < 64 && LG >= 0 && LG < 16, "waitcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (LG << 8));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One stage of the main loop.  Stage j's fragments (both k steps) were read
+// during stage j-1 into register sets U0, U1; this stage reads stage j+1's
+// into R0, R1 while its 32 MFMAs issue, and refills the buffer of stage j-1
+// with stage `refill_step` (A half during the first k step, B half during
+// the second).
+//  - The barrier at the start makes stage j+1 visible (WAIT_OUT: this
+//    thread's DMA instructions that may still be in flight, those issued
+//    after stage j+1's) and frees stage j-1's buffer: every wave finished
+//    its reads of stage j-1 before the LDS reads of stage j it issued last,
+//    and LDS reads complete in order, so the wait may leave this stage's own
+//    2*NR reads outstanding (capped by the 4-bit lgkmcnt field).
+//  - HAS_NEXT: there is a stage j+1.  REFILL: there is a stage to issue.
+// Instruction order is pinned per k step: LDS reads and DMAs spread evenly
+// between the 16 MFMAs.  A DMA issue can stall the wave while the address
+// unit is busy, and a stalled wave issues no MFMA, so no two DMAs sit next
+// to each other.
 template <int NR, int NV>
 __device__ __forceinline__ void interleave_step() {
-  // 16 MFMAs; NR LDS reads and NV DMAs distributed across them.
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
@@ -280,53 +301,27 @@ __device__ __forceinline__ void interleave_step() {
   }
 }
 
-#ifndef FLCE_SPREAD_REFILL
-#define FLCE_SPREAD_REFILL 1
-#endif
-// Refill placement: 0 = all of a stage's DMAs in its first k step, 1 = the A
-// half in the first, the B half in the second.
-constexpr bool kSpreadRefill = FLCE_SPREAD_REFILL != 0;
-// DMA instructions of the refill still outstanding at a hand-over barrier
-// beyond the next-but-one stage.
-constexpr int kRefillOutAtBarrier = kSpreadRefill ? LOADS_PER_TILE : LOADS_PER_STAGE;
-
-template <bool A_KMAJOR, bool B_KMAJOR, int WAIT_OUT, bool REFILL, bool LAST, class LA, class LB>
-__device__ __forceinline__ void stage_compute(bf16* cur, bf16* nxt, bf16* refill, int refill_step, const LA& la,
-                                              const LB& lb, int wave, int wm, int wn, int lane, bf16x8 (&fa)[2][4],
-                                              bf16x8 (&fb)[2][4], f32x16 (&acc)[4][4]) {
+template <bool A_KMAJOR, bool B_KMAJOR, int WAIT_OUT, bool HAS_NEXT, bool REFILL, int U0, int U1, int R0, int R1,
+          class LA, class LB>
+__device__ __forceinline__ void stage_compute(bf16* nxt, bf16* refill, int refill_step, const LA& la, const LB& lb,
+                                              int wave, int wm, int wn, int lane, bf16x8 (&fa)[4][4],
+                                              bf16x8 (&fb)[4][4], f32x16 (&acc)[4][4]) {
   constexpr int NR = frag_reads<A_KMAJOR, B_KMAJOR>();
-  constexpr int NV0 = REFILL ? (kSpreadRefill ? LOADS_PER_TILE : LOADS_PER_STAGE) : 0;
-  constexpr int NV1 = REFILL && kSpreadRefill ? LOADS_PER_TILE : 0;
-  static_assert(SUB == 2, "two k steps per stage");
-  // k step 0: next step's fragments, (part of) the refill, 16 MFMAs.
-  read_frags<A_KMAJOR, B_KMAJOR>(cur, 1, wm, wn, lane, fa[1], fb[1]);
-  if constexpr (REFILL) {
-    la.issue(refill, refill_step * BK, wave);
-    if constexpr (!kSpreadRefill) lb.issue(refill + TILE_ELEMS, refill_step * BK, wave);
+  constexpr int LG = 2 * NR < 15 ? 2 * NR : 15;
+  constexpr int NRD = HAS_NEXT ? NR : 0;
+  constexpr int NV = REFILL ? LOADS_PER_TILE : 0;
+  if constexpr (HAS_NEXT) {
+    stage_barrier_lg<WAIT_OUT, LG>();
+    read_frags<A_KMAJOR, B_KMAJOR>(nxt, 0, wm, wn, lane, fa[R0], fb[R0]);
   }
-  mfma_step(fa[0], fb[0], acc);
-  interleave_step<NR, NV0>();
+  if constexpr (REFILL) la.issue(refill, refill_step * BK, wave);
+  mfma_step(fa[U0], fb[U0], acc);
+  interleave_step<NRD, NV>();
   __builtin_amdgcn_sched_barrier(0);
-  // k step 1: hand over to the next stage, (the rest of) the refill, then
-  // the last 16 MFMAs.
-  if constexpr (!LAST) {
-    stage_barrier<WAIT_OUT>();
-    read_frags<A_KMAJOR, B_KMAJOR>(nxt, 0, wm, wn, lane, fa[0], fb[0]);
-    if constexpr (NV1 > 0) lb.issue(refill + TILE_ELEMS, refill_step * BK, wave);
-    mfma_step(fa[1], fb[1], acc);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NR, 0);
-    if constexpr (NV1 > 0) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        if ((i & 3) == 0) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
-      }
-    } else {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 16, 0);
-    }
-  } else {
-    mfma_step(fa[1], fb[1], acc);
-  }
+  if constexpr (HAS_NEXT) read_frags<A_KMAJOR, B_KMAJOR>(nxt, 1, wm, wn, lane, fa[R1], fb[R1]);
+  if constexpr (REFILL) lb.issue(refill + TILE_ELEMS, refill_step * BK, wave);
+  mfma_step(fa[U1], fb[U1], acc);
+  interleave_step<NRD, NV>();
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -335,14 +330,19 @@ __device__ __forceinline__ void stage_compute(bf16* cur, bf16* nxt, bf16* refill
 // 32x32 block at rows wm*128 + 32*mb, columns wn*128 + 32*nb of the tile.
 //
 // Stage j lives in buffer j % 4.  Stages 0..2 are issued up front; stage
-// it+3 is issued during stage it into the buffer of stage it-1, so three
-// stages are always in flight or resident and a DMA has about two stages of
-// MFMA time to land.
+// j+3 is issued during stage j into the buffer of stage j-1, so a DMA has
+// about two stages of MFMA time to land.  Fragments are read a whole stage
+// (two k steps) ahead: the transposing LDS reads of MN-major operands take
+// a few hundred cycles under load, more than one k step of MFMAs covers.
+// Stage j's k steps use register sets (2j) % 4 and (2j+1) % 4, so the
+// pattern repeats every two stages and the loop unrolls over the four
+// buffers.
 template <bool A_KMAJOR, bool B_KMAJOR>
 __device__ __forceinline__ void mainloop(const Operand& A, const Operand& B, int m0, int n0, int nk, bf16* s0,
                                          bf16* s1, bf16* s2, bf16* s3, f32x16 (&acc)[4][4]) {
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // Wave-uniform in an SGPR, so LDS destinations of the DMAs are scalar.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int wm = wave >> 1;
   const int wn = wave & 1;
@@ -361,28 +361,35 @@ __device__ __forceinline__ void mainloop(const Operand& A, const Operand& B, int
   };
   constexpr int L = LOADS_PER_STAGE;
 
-  // Prologue: stages 0..2 in flight, then wait for stage 0.
+  // Prologue: stages 0..2 in flight; stage 0's fragments read.
   dma(s0, 0);
   dma(s1, 1);
   dma(s2, 2);
   stage_barrier<2 * L>();
-  bf16x8 fa[2][4], fb[2][4];
+  bf16x8 fa[4][4], fb[4][4];
   read_frags<A_KMAJOR, B_KMAJOR>(s0, 0, wm, wn, lane, fa[0], fb[0]);
+  read_frags<A_KMAJOR, B_KMAJOR>(s0, 1, wm, wn, lane, fa[1], fb[1]);
 
-  // At the hand-over barrier of stage it, stage it+1 must have landed; still
-  // in flight may be stage it+2 and what was issued of stage it+3.
+  // At the barrier of stage it+J, stage it+J+1 must have landed; stage
+  // it+J+2 may still be in flight.
+#define FLCE_STAGE(J, REFILL, HAS_NEXT, WAIT)                                                                   \
+  stage_compute<A_KMAJOR, B_KMAJOR, WAIT, HAS_NEXT, REFILL, (2 * (J)) % 4, (2 * (J) + 1) % 4, (2 * (J) + 2) % 4, \
+                (2 * (J) + 3) % 4>((J) == 0 ? s1 : (J) == 1 ? s2 : (J) == 2 ? s3 : s0,                           \
+                                   (J) == 0 ? s3 : (J) == 1 ? s0 : (J) == 2 ? s1 : s2, it + (J) + 3, la, lb, wave, \
+                                   wm, wn, lane, fa, fb, acc)
   int it = 0;
   for (; it + NST < nk; it += NST) {
-    stage_compute<A_KMAJOR, B_KMAJOR, L + kRefillOutAtBarrier, true, false>(s0, s1, s3, it + 3, la, lb, wave, wm, wn, lane, fa, fb, acc);
-    stage_compute<A_KMAJOR, B_KMAJOR, L + kRefillOutAtBarrier, true, false>(s1, s2, s0, it + 4, la, lb, wave, wm, wn, lane, fa, fb, acc);
-    stage_compute<A_KMAJOR, B_KMAJOR, L + kRefillOutAtBarrier, true, false>(s2, s3, s1, it + 5, la, lb, wave, wm, wn, lane, fa, fb, acc);
-    stage_compute<A_KMAJOR, B_KMAJOR, L + kRefillOutAtBarrier, true, false>(s3, s0, s2, it + 6, la, lb, wave, wm, wn, lane, fa, fb, acc);
+    FLCE_STAGE(0, true, true, L);
+    FLCE_STAGE(1, true, true, L);
+    FLCE_STAGE(2, true, true, L);
+    FLCE_STAGE(3, true, true, L);
   }
   // Last four stages: one refill left, then the in-flight count drains.
-  stage_compute<A_KMAJOR, B_KMAJOR, L + kRefillOutAtBarrier, true, false>(s0, s1, s3, it + 3, la, lb, wave, wm, wn, lane, fa, fb, acc);
-  stage_compute<A_KMAJOR, B_KMAJOR, L, false, false>(s1, s2, s0, 0, la, lb, wave, wm, wn, lane, fa, fb, acc);
-  stage_compute<A_KMAJOR, B_KMAJOR, 0, false, false>(s2, s3, s1, 0, la, lb, wave, wm, wn, lane, fa, fb, acc);
-  stage_compute<A_KMAJOR, B_KMAJOR, 0, false, true>(s3, s0, s2, 0, la, lb, wave, wm, wn, lane, fa, fb, acc);
+  FLCE_STAGE(0, true, true, L);
+  FLCE_STAGE(1, false, true, L);
+  FLCE_STAGE(2, false, true, 0);
+  FLCE_STAGE(3, false, false, 0);
+#undef FLCE_STAGE
   stage_barrier<0>();
 }
 
