@@ -23,7 +23,9 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 flop/clk/CU, dense bf16 MFMA
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 flop/clk/CU, dense bf16 MFMA (MI355X published)
+MI355X_CLOCK_GHZ = 2.4      # published peak engine clock
+FLOP_PER_CLK_CU = 4096      # dense bf16 MFMA, per compute unit
 METRIC = "fused linear-CE fwd+bwd tokens/sec on 1 MI355X; % of bf16 MFMA peak"
 
 
@@ -127,16 +129,27 @@ def main():
     torch.cuda.synchronize()
 
     trace = L.LaunchTrace(capacity=max(64, 64 * args.steps)).start()
+    # Events at each step's start, between its forward and backward, and at
+    # its end (the library launches on torch's current stream).
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        ev[i][0].record()
+        L.flce_forward(p, X, W, y, loss, lse, workspace=ws)
+        ev[i][1].record()
+        L.flce_backward(p, X, W, y, lse, g, dX, dW, workspace=ws)
+        ev[i][2].record()
     e1.record()
     torch.cuda.synchronize()
     trace.stop()
     ms = e0.elapsed_time(e1) / args.steps
+    step_ms = sorted(a.elapsed_time(c) for a, _, c in ev)
+    fwd_ms = sorted(a.elapsed_time(b) for a, b, _ in ev)
+    bwd_ms = sorted(b.elapsed_time(c) for _, b, c in ev)
+    med = lambda v: v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2])
     records = trace.records()
 
     # The library prices a contraction launch at 2*T*rows*H; only the Tv
@@ -172,10 +185,14 @@ def main():
         "flops_per_launch": dom["flops"] / dom["launches"],
     }
     credited = 8.0 * Tv * Vu * H
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    peak_dev = n_cu * MI355X_CLOCK_GHZ * FLOP_PER_CLK_CU / 1e3
     tokens_per_s = T / (ms * 1e-3)
     pct_peak = credited / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12) * 100.0
     log(f"step {ms:.3f} ms  {tokens_per_s:,.0f} tokens/s  {pct_peak:.1f}% of bf16 peak "
         f"(credited {credited / 1e12:.2f} TFLOP)  loss={loss.item():.6g}")
+    log(f"  per step: median {med(step_ms):.3f} ms, min {step_ms[0]:.3f} ms; forward {med(fwd_ms):.3f} ms, "
+        f"backward {med(bwd_ms):.3f} ms (medians); {n_cu} CUs -> peak {peak_dev:.1f} TFLOP/s")
 
     if args.calibration_copy_mib > 0:
         n = args.calibration_copy_mib << 20
@@ -213,8 +230,13 @@ def main():
             "softcap": w.softcap, "reduction": w.reduction,
             "num_label_tokens": inp["num_label_tokens"],
             "credited_tflop_per_step": round(credited / 1e12, 3),
+            "model_tflop_per_step": round(6.0 * Tv * Vu * H / 1e12, 3),
             "label_tokens_per_s": round(Tv / (ms * 1e-3), 1),
         },
+        "step_ms": {"median": round(med(step_ms), 4), "min": round(step_ms[0], 4),
+                    "fwd_median": round(med(fwd_ms), 4), "bwd_median": round(med(bwd_ms), 4)},
+        "peak_from_device": {"compute_units": n_cu, "clock_ghz": MI355X_CLOCK_GHZ,
+                             "tflops": round(peak_dev, 1)},
         "roofline": roofline,
         "kernel_source_hash": kernel_source_hash(),
         "cpu_baseline": cpu,

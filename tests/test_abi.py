@@ -62,6 +62,21 @@ def test_workspace_size_bounds():
     assert code == _lib.FLCE_OK and ws3 < 8192 * 256000 * 2
     code, ws0 = _ws(make_problem(0, 128, 1000))
     assert code == _lib.FLCE_OK and ws0 == 0
+    # sparse-label packed batch and long peaked head
+    for T, H, V in ((16384, 5120, 152064), (65536, 8192, 128256)):
+        code, w = _ws(make_problem(T, H, V, softcap=30.0))
+        assert code == _lib.FLCE_OK and w < T * V * 2
+
+
+def test_library_source_allocates_no_device_memory():
+    """The caller owns every buffer: no allocation or free call in the HIP
+    sources (the workspace comes in as an argument)."""
+    csrc = os.path.join(ROOT, "lm_head_cross_amd", "csrc")
+    banned = re.compile(r"\b(hipMalloc\w*|hipFree\w*|hipHostMalloc|hipExtMallocWithFlags|hipMemAlloc\w*|malloc|new\s+\w)")
+    for name in sorted(os.listdir(csrc)):
+        text = open(os.path.join(csrc, name)).read()
+        code = re.sub(r"//[^\n]*|/\*.*?\*/", "", text, flags=re.S)
+        assert not banned.search(code), (name, banned.search(code).group(0))
 
 
 @pytest.mark.parametrize("kw,expect", [

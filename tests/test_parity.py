@@ -225,3 +225,30 @@ def test_workload_full_size(key):
     say(f"  dX relL2 over {len(tok)} rows = {e_dx:.3g}; dW relL2 over {len(voc)} rows = {e_dw:.3g}")
     assert e_dx <= TOL_GRAD_REL_L2
     assert e_dw <= TOL_GRAD_REL_L2
+
+
+def test_no_logits_sized_allocation():
+    """Forward + backward at the llama3-8b head shape with the outputs already
+    allocated: the call's extra device memory (the workspace the binding
+    allocates) stays below one bf16 [T, Vu] logits buffer."""
+    import lm_head_cross_amd as L
+    w = WORKLOADS[2]
+    d = torch.device("cuda:0")
+    inp = make_inputs(w, device="cuda:0")
+    p = L.make_problem(w.T, w.H, w.V, w.Vu, w.softcap, inp["ignore_index"], w.reduction, inp["num_label_tokens"])
+    loss = torch.empty((), device=d)
+    lse = torch.empty(w.T, device=d)
+    dX = torch.empty_like(inp["hidden"])
+    dW = torch.empty((w.V, w.H), device=d)
+    g = torch.ones((), device=d)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(d)
+    base = torch.cuda.memory_allocated(d)
+    L.flce_forward(p, inp["hidden"], inp["weight"], inp["labels"], loss, lse)
+    L.flce_backward(p, inp["hidden"], inp["weight"], inp["labels"], lse, g, dX, dW)
+    torch.cuda.synchronize()
+    extra = torch.cuda.max_memory_allocated(d) - base
+    say(f"  extra device memory {extra / 2**20:.1f} MiB, workspace {L.flce_workspace_size(p) / 2**20:.1f} MiB, "
+        f"bf16 [T, Vu] {w.T * w.Vu * 2 / 2**20:.1f} MiB")
+    assert extra < w.T * w.Vu * 2
+    assert math.isfinite(loss.item())
