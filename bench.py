@@ -10,6 +10,11 @@ work (8 Tv Vu H flops: projection, recompute, dX and dW) reaches, a roofline
 entry for the dominant kernel from HIP events recorded around each of its
 launches inside the timed region, and the CPU oracle timed on a bounded slice
 of the same workload.
+
+    python bench.py --path chunked_ce [--ce-workload ce2]
+
+times the cross-entropy over given logits (chunked_ce_forward +
+chunked_ce_backward) instead, against the HBM roofline.
 """
 from __future__ import annotations
 
@@ -90,12 +95,19 @@ def main():
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch of the dominant kernel, from rocprofv3 counters")
+    ap.add_argument("--path", choices=("flce", "chunked_ce"), default="flce",
+                    help="flce: fused linear cross-entropy (the default workload); chunked_ce: cross-entropy "
+                         "over given logits")
+    ap.add_argument("--ce-workload", default="ce2", help="logits-input workload for --path chunked_ce")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the fused linear cross-entropy path is built and timed on a "
               "single MI355X; runs on more than one GPU are not supported.", file=sys.stderr)
         sys.exit(2)
+
+    if args.path == "chunked_ce":
+        return bench_chunked_ce(args)
 
     import torch
 
@@ -238,6 +250,126 @@ def main():
         "peak_from_device": {"compute_units": n_cu, "clock_ghz": MI355X_CLOCK_GHZ,
                              "tflops": round(peak_dev, 1)},
         "roofline": roofline,
+        "kernel_source_hash": kernel_source_hash(),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_ce(inp, n_rows):
+    """Time the logits-input oracle (fwd + bwd) on the first n_rows positions."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"),
+                      default=os.cpu_count())
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    z = oracle.to_f64(inp["logits"][:n_rows].cpu())
+    y = inp["labels"][:n_rows].cpu().numpy()
+    m = None if inp["mask"] is None else inp["mask"][:n_rows].cpu().numpy()
+    p = oracle.CEProblem(ignore_index=inp["ignore_index"], reduction=inp["reduction"],
+                         num_label_tokens=inp["num_label_tokens"])
+    t0 = time.perf_counter()
+    oracle.ce_forward(z, y, p, mask=m)
+    oracle.ce_backward(z, y, p, mask=m)
+    dt = time.perf_counter() - t0
+    return {"value": n_rows / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n_rows} positions of the workload, fwd+bwd over the full vocabulary "
+                      f"(fp64 numpy, {dt:.1f} s)"}
+
+
+def bench_chunked_ce(args):
+    """Cross-entropy over given logits: forward + backward per step."""
+    import torch
+
+    import lm_head_cross_amd as L
+    from workloads import LOGIT_WORKLOADS, make_logit_inputs
+
+    w = LOGIT_WORKLOADS[args.ce_workload]
+    dev = torch.device("cuda:0")
+    log(f"logits workload {w.key}: {w.name}")
+    inp = make_logit_inputs(w, device="cuda:0")
+    z, y, m = inp["logits"], inp["labels"], inp["mask"]
+    T, V = z.shape
+    Tv = inp["n_valid"]
+    esz = z.element_size()
+    p = L.make_ce_problem(T, V, z.dtype, inp["ignore_index"], w.reduction, inp["num_label_tokens"])
+    ws = L.alloc_ce_workspace(p, dev)
+    loss = torch.empty((), device=dev)
+    lse = torch.empty(T, device=dev)
+    g = torch.ones((), device=dev)
+    dz = torch.empty_like(z)
+
+    def step():
+        L.chunked_ce_forward(p, z, y, loss, lse, mask=m, workspace=ws)
+        L.chunked_ce_backward(p, z, y, lse, g, dz, mask=m, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    trace = L.LaunchTrace(capacity=max(64, 8 * args.steps)).start()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    trace.stop()
+    ms = e0.elapsed_time(e1) / args.steps
+    # Algorithmic bytes per launch: the forward reads the counted rows once;
+    # the backward reads them and writes every gradient row.
+    alg = {"ce_forward": Tv * V * esz + T * 8, "ce_backward": Tv * V * esz + T * V * esz + T * 8}
+    kinds = {}
+    for kind, kms, _ in trace.records():
+        k = kinds.setdefault(kind, {"launches": 0, "ms": 0.0})
+        k["launches"] += 1
+        k["ms"] += kms
+    for name, k in sorted(kinds.items(), key=lambda kv: -kv[1]["ms"]):
+        gbs = alg[name] * k["launches"] / (k["ms"] * 1e-3) / 1e9 if name in alg else 0.0
+        log(f"  {name:12s} launches={k['launches']:5d} total={k['ms'] / args.steps:8.3f} ms/step "
+            f"avg={k['ms'] / k['launches'] * 1e3:9.1f} us" + (f"  {gbs:7.1f} GB/s (algorithmic)" if gbs else ""))
+    dom_name, dom = max(((n, k) for n, k in kinds.items() if n in alg), key=lambda kv: kv[1]["ms"])
+    achieved = alg[dom_name] * dom["launches"] / (dom["ms"] * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        with open(args.traffic_json) as f:
+            tj = json.load(f)
+        entry = tj.get(w.key, {}).get(dom_name)
+        if entry and tj.get("kernel_source_hash") == kernel_source_hash():
+            traffic = entry.get("bytes_per_launch")
+    step_bytes = alg["ce_forward"] + alg["ce_backward"]
+    log(f"step {ms:.3f} ms  {T / (ms * 1e-3):,.0f} tokens/s  {step_bytes / (ms * 1e-3) / 1e9:.0f} GB/s "
+        f"algorithmic ({step_bytes / (ms * 1e-3) / 8e12 * 100:.1f}% of HBM peak)  loss={loss.item():.6g}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_ce(inp, 256)
+        log(f"  oracle {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
+    line = {
+        "metric": "chunked CE (logits input) fwd+bwd tokens/sec on 1 MI355X; % of HBM peak",
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {torch.bfloat16: "bf16", torch.float32: "fp32"}[z.dtype],
+        "data": "synthetic",
+        "pct_of_hbm_peak": round(step_bytes / (ms * 1e-3) / 8e12 * 100, 2),
+        "config": {"workload": w.name, "tokens": T, "vocab": V, "valid_tokens": Tv, "reduction": w.reduction,
+                   "mask": m is not None, "algorithmic_gb_per_step": round(step_bytes / 1e9, 3)},
+        "roofline": {"kernel": dom_name, "bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0,
+                     "unit": "GB/s", "frac": round(achieved / 8000.0, 4), "traffic": traffic,
+                     "avg_launch_us": round(dom["ms"] / dom["launches"] * 1e3, 1),
+                     "bytes_per_launch": alg[dom_name]},
         "kernel_source_hash": kernel_source_hash(),
         "cpu_baseline": cpu,
     }

@@ -73,7 +73,8 @@ typedef enum flce_reduction {
 } flce_reduction_t;
 
 typedef enum flce_dtype {
-  FLCE_DTYPE_BF16 = 0
+  FLCE_DTYPE_BF16 = 0,
+  FLCE_DTYPE_FP32 = 1
 } flce_dtype_t;
 
 /*
@@ -91,8 +92,8 @@ typedef enum flce_dtype {
  * num_label_tokens  > 0: divide the summed loss by this count whatever the
  *                   reduction (linear_ce page, forward argument
  *                   num_label_tokens); < 0: not given.  0 is invalid.
- * weight_dtype      FLCE_DTYPE_BF16 (the only head dtype accepted; an fp32
- *                   head is rounded to bf16 by the caller).
+ * weight_dtype      FLCE_DTYPE_BF16 (the only head dtype accepted here; an
+ *                   fp32 head is rounded to bf16 by the caller).
  */
 typedef struct flce_problem {
   int64_t num_tokens;
@@ -190,7 +191,9 @@ typedef enum flce_kernel_kind {
   FLCE_KERNEL_RECOMPUTE_G = 5,  /* backward logit recompute -> G chunk         */
   FLCE_KERNEL_DWEIGHT = 6,      /* dW rows of a chunk = G^T X                  */
   FLCE_KERNEL_DHIDDEN = 7,      /* dH += G W[chunk]                            */
-  FLCE_KERNEL_AUX = 8           /* zero fills, scale, rounding                 */
+  FLCE_KERNEL_AUX = 8,          /* zero fills, scale, rounding                 */
+  FLCE_KERNEL_CE_FORWARD = 9,   /* chunked CE: per-row lse and loss            */
+  FLCE_KERNEL_CE_BACKWARD = 10  /* chunked CE: per-row logits gradient         */
 } flce_kernel_kind_t;
 
 /*

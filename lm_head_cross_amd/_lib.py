@@ -1,4 +1,5 @@
-"""ctypes loader for ``libflce.so`` and the C structures of include/flce.h.
+"""ctypes loader for ``libflce.so`` and the C structures of include/flce.h and
+include/chunked_ce.h.
 
 Argument marshalling only: every step of the computation runs in the HIP
 library.  Loading fails loudly when the library has not been built.
@@ -19,12 +20,14 @@ FLCE_DEVICE_BAD_LABEL = 1
 FLCE_REDUCTION_SUM = 0
 FLCE_REDUCTION_MEAN = 1
 FLCE_DTYPE_BF16 = 0
+FLCE_DTYPE_FP32 = 1
 
 EXPORTED = ("flce_status_string", "flce_version", "flce_workspace_size", "flce_forward", "flce_backward",
-            "flce_round_to_bf16", "flce_trace_start", "flce_trace_stop", "flce_trace_count", "flce_trace_get")
+            "flce_round_to_bf16", "flce_trace_start", "flce_trace_stop", "flce_trace_count", "flce_trace_get",
+            "chunked_ce_workspace_size", "chunked_ce_forward", "chunked_ce_backward", "chunked_ce_mask_labels")
 
 KERNEL_KINDS = ("compact", "gather", "proj_lse", "combine", "finalize", "recompute_g", "dweight", "dhidden",
-                "aux")
+                "aux", "ce_forward", "ce_backward")
 
 
 class Problem(ctypes.Structure):
@@ -40,6 +43,20 @@ class Problem(ctypes.Structure):
         ("ignore_index", ctypes.c_int64),
         ("num_label_tokens", ctypes.c_int64),
         ("weight_dtype", ctypes.c_int32),
+    ]
+
+
+class CEProblem(ctypes.Structure):
+    """chunked_ce_problem_t."""
+
+    _fields_ = [
+        ("num_tokens", ctypes.c_int64),
+        ("vocab", ctypes.c_int64),
+        ("ignore_index", ctypes.c_int64),
+        ("reduction", ctypes.c_int32),
+        ("num_label_tokens", ctypes.c_int64),
+        ("logits_dtype", ctypes.c_int32),
+        ("chunk_len", ctypes.c_int64),
     ]
 
 
@@ -82,6 +99,16 @@ def load() -> ctypes.CDLL:
                                    ctypes.POINTER(ctypes.c_double)]
     lib.flce_round_to_bf16.restype = ctypes.c_int
     lib.flce_round_to_bf16.argtypes = [vp, vp, ctypes.c_int64, vp]
+    C = ctypes.POINTER(CEProblem)
+    i32 = ctypes.c_int32
+    lib.chunked_ce_workspace_size.restype = ctypes.c_int
+    lib.chunked_ce_workspace_size.argtypes = [C, ctypes.POINTER(ctypes.c_size_t)]
+    lib.chunked_ce_forward.restype = ctypes.c_int
+    lib.chunked_ce_forward.argtypes = [C, vp, vp, vp, i32, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.chunked_ce_backward.restype = ctypes.c_int
+    lib.chunked_ce_backward.argtypes = [C, vp, vp, vp, i32, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.chunked_ce_mask_labels.restype = ctypes.c_int
+    lib.chunked_ce_mask_labels.argtypes = [vp, vp, i32, ctypes.c_int64, ctypes.c_int64, vp]
     _lib = lib
     return lib
 

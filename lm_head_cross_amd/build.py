@@ -12,7 +12,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", "flce.hip")]
+SOURCES = [os.path.join(PKG, "csrc", "flce.hip"), os.path.join(PKG, "csrc", "chunked_ce.hip")]
 OUTPUT = os.path.join(PKG, "libflce.so")
 ARCH = "gfx950"
 

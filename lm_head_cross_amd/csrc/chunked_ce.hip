@@ -1,0 +1,464 @@
+// Cross-entropy over given logits ("nemo_automodel.components.loss.chunked_ce",
+// ChunkedCrossEntropy and _ChunkedCrossEntropySum) for gfx950.
+//
+// The work is one pass over the logits per direction, so the roofline is HBM
+// bandwidth.  One 256-thread workgroup owns one row (position):
+//  - forward: every lane keeps a running (max, sum of exp(x - max)) over the
+//    16-byte vectors it reads, lanes merge in a fixed butterfly order and the
+//    four waves in wave order, giving lse[t] in fp32; the label logit is read
+//    once.  Per-row losses are summed in fp64 in a fixed order by one block.
+//  - backward: each element becomes (g/D)(exp(x - lse[t]) - [v == y]) in the
+//    logits' dtype (bf16 with round-to-nearest-even), streamed straight back.
+// Rows of ignored positions are never read; their gradient rows are written
+// as zeros.  Rows need not be 16-byte aligned (any V): each row is split into
+// a scalar head up to the first 16-byte boundary, 16-byte vectors, and a
+// scalar tail.
+//
+// Results are deterministic: no atomics take part in any sum.
+
+#include <stdint.h>
+
+#include "../../include/chunked_ce.h"
+#include "device_common.hpp"
+#include "host_common.hpp"
+
+namespace flce {
+namespace cce {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kFinalizeThreads = 1024;
+
+// Whether position t counts under the mask (absent mask: always).
+__device__ __forceinline__ bool mask_keeps(const void* mask, int elem_bytes, int64_t t) {
+  if (!mask) return true;
+  switch (elem_bytes) {
+    case 1: return static_cast<const uint8_t*>(mask)[t] != 0;
+    case 2: return static_cast<const uint16_t*>(mask)[t] != 0;
+    case 4: return static_cast<const uint32_t*>(mask)[t] != 0;
+    default: return static_cast<const uint64_t*>(mask)[t] != 0;
+  }
+}
+
+// Label of position t after the mask, or -1 if the position does not count.
+// A label outside [0, V) at a kept position is flagged and not counted.
+__device__ __forceinline__ int64_t counted_label(const int64_t* labels, const void* mask, int mask_bytes, int64_t t,
+                                                 int64_t V, int64_t ignore_index, int32_t* status) {
+  if (!mask_keeps(mask, mask_bytes, t)) return -1;
+  const int64_t y = labels[t];
+  if (y == ignore_index) return -1;
+  if (y < 0 || y >= V) {
+    if (status) atomicOr(status, FLCE_DEVICE_BAD_LABEL);
+    return -1;
+  }
+  return y;
+}
+
+// Element loads and stores for the two logits dtypes.
+template <class T>
+struct Elt;
+template <>
+struct Elt<bf16> {
+  static constexpr int kPerVec = 8;
+  static __device__ __forceinline__ float load(const bf16* p) { return (float)*p; }
+  static __device__ __forceinline__ void store(bf16* p, float v) { *p = (bf16)v; }
+  static __device__ __forceinline__ void unpack(const uint4& v, float* x) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+      x[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+    }
+  }
+  static __device__ __forceinline__ uint4 pack(const float (&x)[8]) {
+    bf16x8 o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = (bf16)x[i];
+    return __builtin_bit_cast(uint4, o);
+  }
+};
+template <>
+struct Elt<float> {
+  static constexpr int kPerVec = 4;
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ void store(float* p, float v) { *p = v; }
+  static __device__ __forceinline__ void unpack(const uint4& v, float* x) {
+    x[0] = __builtin_bit_cast(float, v.x);
+    x[1] = __builtin_bit_cast(float, v.y);
+    x[2] = __builtin_bit_cast(float, v.z);
+    x[3] = __builtin_bit_cast(float, v.w);
+  }
+  static __device__ __forceinline__ uint4 pack(const float (&x)[4]) {
+    return make_uint4(__builtin_bit_cast(uint32_t, x[0]), __builtin_bit_cast(uint32_t, x[1]),
+                      __builtin_bit_cast(uint32_t, x[2]), __builtin_bit_cast(uint32_t, x[3]));
+  }
+};
+
+// Elements of a row before its first 16-byte boundary (the row may start
+// anywhere on an element boundary).
+template <class T>
+__device__ __forceinline__ int64_t row_head(const T* row, int64_t V) {
+  const int64_t h = (int64_t)(((16u - (reinterpret_cast<uintptr_t>(row) & 15u)) & 15u) / sizeof(T));
+  return h < V ? h : V;
+}
+
+// Running (max, sum of exp(x - max)) of one lane, the max kept in base-2
+// units (m2 = max * log2 e) so each element costs one fma and one exp2.
+struct Online {
+  float m2 = kNegInf;
+  float s = 0.0f;
+  template <int N>
+  __device__ __forceinline__ void add(const float (&x)[N]) {
+    float gm = x[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) gm = __builtin_fmaxf(gm, x[i]);
+    const float g2 = gm * kLog2e;
+    if (g2 > m2) {
+      s *= __builtin_amdgcn_exp2f(m2 - g2);
+      m2 = g2;
+    }
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < N; ++i) a += __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], kLog2e, -m2));
+    s += a;
+  }
+  __device__ __forceinline__ void merge(float om2, float os) {
+    const float mx = __builtin_fmaxf(m2, om2);
+    if (mx == kNegInf) return;
+    s = s * __builtin_amdgcn_exp2f(m2 - mx) + os * __builtin_amdgcn_exp2f(om2 - mx);
+    m2 = mx;
+  }
+};
+
+// Forward: per counted row, lse and loss; row_loss[t] is 0 for ignored rows.
+template <class T>
+__global__ __launch_bounds__(kThreads) void k_row_forward(const T* __restrict__ logits, int64_t V,
+                                                          const int64_t* __restrict__ labels, const void* mask,
+                                                          int mask_bytes, int64_t ignore_index, float* lse_out,
+                                                          float* tl_out, float* row_loss, int32_t* status) {
+  __shared__ float red[2][kWaves];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t y = counted_label(labels, mask, mask_bytes, t, V, ignore_index, tid == 0 ? status : nullptr);
+  if (y < 0) {
+    if (tid == 0) {
+      lse_out[t] = 0.0f;
+      if (tl_out) tl_out[t] = 0.0f;
+      row_loss[t] = 0.0f;
+    }
+    return;
+  }
+  constexpr int E = Elt<T>::kPerVec;
+  const T* row = logits + t * V;
+  const int64_t head = row_head(row, V);
+  const int64_t nvec = (V - head) / E;
+  const int64_t tail0 = head + nvec * E;
+  const uint4* vrow = reinterpret_cast<const uint4*>(row + head);
+
+  Online o;
+  for (int64_t i = tid; i < head; i += kThreads) {
+    const float x[1] = {Elt<T>::load(row + i)};
+    o.add(x);
+  }
+  int64_t i = tid;
+  for (; i + 3 * kThreads < nvec; i += 4 * kThreads) {
+    const uint4 v0 = vrow[i], v1 = vrow[i + kThreads], v2 = vrow[i + 2 * kThreads], v3 = vrow[i + 3 * kThreads];
+    float x[4 * E];
+    Elt<T>::unpack(v0, x);
+    Elt<T>::unpack(v1, x + E);
+    Elt<T>::unpack(v2, x + 2 * E);
+    Elt<T>::unpack(v3, x + 3 * E);
+    o.add(x);
+  }
+  for (; i < nvec; i += kThreads) {
+    float x[E];
+    Elt<T>::unpack(vrow[i], x);
+    o.add(x);
+  }
+  for (int64_t j = tail0 + tid; j < V; j += kThreads) {
+    const float x[1] = {Elt<T>::load(row + j)};
+    o.add(x);
+  }
+  // Lanes, then waves, in a fixed order.
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) o.merge(__shfl_xor(o.m2, off, 64), __shfl_xor(o.s, off, 64));
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = o.m2;
+    red[1][tid >> 6] = o.s;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    Online a;
+    for (int w = 0; w < kWaves; ++w) a.merge(red[0][w], red[1][w]);
+    const float lse = (a.m2 + __builtin_amdgcn_logf(a.s)) * kLn2;
+    const float l = lse - Elt<T>::load(row + y);
+    lse_out[t] = lse;
+    if (tl_out) tl_out[t] = l;
+    row_loss[t] = l;
+  }
+}
+
+// Normaliser of the summed loss from the counted-position count.
+__device__ __forceinline__ double divisor(int reduction, int64_t num_label_tokens, int64_t count) {
+  if (num_label_tokens > 0) return (double)num_label_tokens;
+  if (reduction == FLCE_REDUCTION_MEAN) return (double)count;
+  return 1.0;
+}
+
+// Per-thread contiguous ranges of positions: the fp64 loss sum and the count
+// of counted positions, then a fixed pairwise tree.  One block.
+__global__ __launch_bounds__(kFinalizeThreads) void k_finalize(const float* __restrict__ row_loss,
+                                                               const int64_t* __restrict__ labels,
+                                                               const void* mask, int mask_bytes, int64_t T,
+                                                               int64_t V, int64_t ignore_index, int reduction,
+                                                               int64_t num_label_tokens, float* loss) {
+  __shared__ double ssum[kFinalizeThreads];
+  __shared__ int64_t scnt[kFinalizeThreads];
+  const int tid = threadIdx.x;
+  const int64_t per = (T + kFinalizeThreads - 1) / kFinalizeThreads;
+  const int64_t t0 = tid * per;
+  const int64_t t1 = t0 + per < T ? t0 + per : T;
+  double s = 0.0;
+  int64_t c = 0;
+  for (int64_t t = t0; t < t1; ++t) {
+    if (counted_label(labels, mask, mask_bytes, t, V, ignore_index, nullptr) >= 0) {
+      s += (double)row_loss[t];
+      ++c;
+    }
+  }
+  ssum[tid] = s;
+  scnt[tid] = c;
+  __syncthreads();
+  for (int off = kFinalizeThreads / 2; off > 0; off >>= 1) {
+    if (tid < off) {
+      ssum[tid] += ssum[tid + off];
+      scnt[tid] += scnt[tid + off];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) *loss = (float)(ssum[0] / divisor(reduction, num_label_tokens, scnt[0]));
+}
+
+// g / D for the backward pass (0 when nothing counts).
+__global__ __launch_bounds__(kFinalizeThreads) void k_scale(const int64_t* __restrict__ labels, const void* mask,
+                                                            int mask_bytes, int64_t T, int64_t V,
+                                                            int64_t ignore_index, int reduction,
+                                                            int64_t num_label_tokens, const float* grad_out,
+                                                            float* scale) {
+  __shared__ int64_t scnt[kFinalizeThreads];
+  const int tid = threadIdx.x;
+  int64_t c = 0;
+  for (int64_t t = tid; t < T; t += kFinalizeThreads)
+    c += counted_label(labels, mask, mask_bytes, t, V, ignore_index, nullptr) >= 0;
+  scnt[tid] = c;
+  __syncthreads();
+  for (int off = kFinalizeThreads / 2; off > 0; off >>= 1) {
+    if (tid < off) scnt[tid] += scnt[tid + off];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const double D = divisor(reduction, num_label_tokens, scnt[0]);
+    *scale = scnt[0] > 0 ? (float)((double)*grad_out / D) : 0.0f;
+  }
+}
+
+// Backward: d_logits[t, v] = scale (exp(x - lse[t]) - [v == y]) for counted
+// rows, 0 for the others.
+template <class T>
+__global__ __launch_bounds__(kThreads) void k_row_backward(const T* __restrict__ logits, int64_t V,
+                                                           const int64_t* __restrict__ labels, const void* mask,
+                                                           int mask_bytes, int64_t ignore_index,
+                                                           const float* __restrict__ lse,
+                                                           const float* __restrict__ scale_p, T* __restrict__ dlogits,
+                                                           int32_t* status) {
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  constexpr int E = Elt<T>::kPerVec;
+  const int64_t y = counted_label(labels, mask, mask_bytes, t, V, ignore_index, tid == 0 ? status : nullptr);
+  const T* row = logits + t * V;
+  T* out = dlogits + t * V;
+  const int64_t head = row_head(out, V);
+  const int64_t nvec = (V - head) / E;
+  const int64_t tail0 = head + nvec * E;
+  uint4* vout = reinterpret_cast<uint4*>(out + head);
+  if (y < 0) {
+    for (int64_t i = tid; i < head; i += kThreads) Elt<T>::store(out + i, 0.0f);
+    for (int64_t i = tid; i < nvec; i += kThreads) vout[i] = make_uint4(0, 0, 0, 0);
+    for (int64_t j = tail0 + tid; j < V; j += kThreads) Elt<T>::store(out + j, 0.0f);
+    return;
+  }
+  const float scale = *scale_p;
+  const float l2 = lse[t] * kLog2e;
+  const uint4* vrow = reinterpret_cast<const uint4*>(row + head);
+  auto grad = [&](float x) { return scale * __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -l2)); };
+  for (int64_t i = tid; i < head; i += kThreads) {
+    const float g = grad(Elt<T>::load(row + i)) - (i == y ? scale : 0.0f);
+    Elt<T>::store(out + i, g);
+  }
+  for (int64_t i = tid; i < nvec; i += kThreads) {
+    float x[E];
+    Elt<T>::unpack(vrow[i], x);
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = grad(x[e]);
+    const int64_t d = y - (head + i * E);
+    if (d >= 0 && d < E) {
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (d == e) x[e] -= scale;
+    }
+    vout[i] = Elt<T>::pack(x);
+  }
+  for (int64_t j = tail0 + tid; j < V; j += kThreads) {
+    const float g = grad(Elt<T>::load(row + j)) - (j == y ? scale : 0.0f);
+    Elt<T>::store(out + j, g);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_mask_labels(int64_t* labels, const void* mask, int mask_bytes, int64_t n,
+                                                      int64_t ignore_index) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n; t += stride)
+    if (!mask_keeps(mask, mask_bytes, t)) labels[t] = ignore_index;
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+
+namespace {
+
+using namespace host;
+
+constexpr size_t kAlign = 256;
+
+int validate(const chunked_ce_problem_t* p) {
+  if (!p) return FLCE_ERR_INVALID_ARG;
+  if (p->num_tokens < 0 || p->vocab <= 0 || p->chunk_len <= 0) return FLCE_ERR_INVALID_ARG;
+  if (p->reduction != FLCE_REDUCTION_SUM && p->reduction != FLCE_REDUCTION_MEAN) return FLCE_ERR_INVALID_ARG;
+  if (p->num_label_tokens == 0) return FLCE_ERR_INVALID_ARG;
+  if (p->logits_dtype != FLCE_DTYPE_BF16 && p->logits_dtype != FLCE_DTYPE_FP32) return FLCE_ERR_UNSUPPORTED;
+  // One workgroup per row: the grid's x extent bounds T.
+  if (p->num_tokens > 0x7FFFFFFF || p->vocab > (int64_t(1) << 40)) return FLCE_ERR_UNSUPPORTED;
+  return FLCE_OK;
+}
+
+bool mask_ok(const void* mask, int32_t bytes) {
+  if (!mask) return true;
+  return (bytes == 1 || bytes == 2 || bytes == 4 || bytes == 8);
+}
+
+size_t workspace_bytes_for(const chunked_ce_problem_t& p) {
+  return p.num_tokens == 0 ? 0 : align_up((size_t)p.num_tokens * 4, kAlign) + kAlign;
+}
+
+int check_ws(const chunked_ce_problem_t& p, void* ws, size_t bytes) {
+  const size_t need = workspace_bytes_for(p);
+  if (need == 0) return FLCE_OK;
+  if (!ws || !aligned(ws, kAlign) || bytes < need) return FLCE_ERR_WORKSPACE;
+  return FLCE_OK;
+}
+
+}  // namespace
+}  // namespace cce
+}  // namespace flce
+
+using namespace flce;
+using namespace flce::cce;
+
+extern "C" {
+
+int chunked_ce_workspace_size(const chunked_ce_problem_t* problem, size_t* bytes) {
+  const int st = validate(problem);
+  if (st != FLCE_OK) return st;
+  if (!bytes) return FLCE_ERR_INVALID_ARG;
+  *bytes = workspace_bytes_for(*problem);
+  return FLCE_OK;
+}
+
+int chunked_ce_forward(const chunked_ce_problem_t* problem, const void* logits, const int64_t* labels,
+                       const void* mask, int32_t mask_elem_bytes, float* loss, float* lse, float* token_loss,
+                       int32_t* device_status, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = validate(problem);
+  if (st != FLCE_OK) return st;
+  const chunked_ce_problem_t p = *problem;
+  const int64_t T = p.num_tokens;
+  if (!loss || !mask_ok(mask, mask_elem_bytes)) return FLCE_ERR_INVALID_ARG;
+  if (T > 0 && (!logits || !labels || !lse)) return FLCE_ERR_INVALID_ARG;
+  if (!aligned(logits, 16) || !aligned(labels, 8) || !aligned(loss, 4) || !aligned(lse, 4) ||
+      !aligned(token_loss, 4) || !aligned(device_status, 4) || (mask && !aligned(mask, mask_elem_bytes)))
+    return FLCE_ERR_UNSUPPORTED;
+  if ((st = check_ws(p, workspace, workspace_bytes)) != FLCE_OK) return st;
+  float* row_loss = static_cast<float*>(workspace);
+  const int mb = mask ? mask_elem_bytes : 0;
+  if (T > 0) {
+    TraceScope tr(FLCE_KERNEL_CE_FORWARD, 0.0, stream);
+    if (p.logits_dtype == FLCE_DTYPE_BF16)
+      hipLaunchKernelGGL(k_row_forward<bf16>, dim3((unsigned)T), dim3(kThreads), 0, stream,
+                         static_cast<const bf16*>(logits), p.vocab, labels, mask, mb, p.ignore_index, lse,
+                         token_loss, row_loss, device_status);
+    else
+      hipLaunchKernelGGL(k_row_forward<float>, dim3((unsigned)T), dim3(kThreads), 0, stream,
+                         static_cast<const float*>(logits), p.vocab, labels, mask, mb, p.ignore_index, lse,
+                         token_loss, row_loss, device_status);
+  }
+  {
+    TraceScope tr(FLCE_KERNEL_AUX, 0.0, stream);
+    hipLaunchKernelGGL(k_finalize, dim3(1), dim3(kFinalizeThreads), 0, stream, (const float*)row_loss, labels, mask,
+                       mb, T, p.vocab, p.ignore_index, (int)p.reduction, p.num_label_tokens, loss);
+  }
+  return launch_status();
+}
+
+int chunked_ce_backward(const chunked_ce_problem_t* problem, const void* logits, const int64_t* labels,
+                        const void* mask, int32_t mask_elem_bytes, const float* lse, const float* grad_out,
+                        void* d_logits, int32_t* device_status, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  int st = validate(problem);
+  if (st != FLCE_OK) return st;
+  const chunked_ce_problem_t p = *problem;
+  const int64_t T = p.num_tokens;
+  if (!grad_out || !mask_ok(mask, mask_elem_bytes)) return FLCE_ERR_INVALID_ARG;
+  if (T == 0) return FLCE_OK;
+  if (!logits || !labels || !lse || !d_logits) return FLCE_ERR_INVALID_ARG;
+  if (!aligned(logits, 16) || !aligned(d_logits, 16) || !aligned(labels, 8) || !aligned(lse, 4) ||
+      !aligned(grad_out, 4) || !aligned(device_status, 4) || (mask && !aligned(mask, mask_elem_bytes)))
+    return FLCE_ERR_UNSUPPORTED;
+  const size_t esz = p.logits_dtype == FLCE_DTYPE_BF16 ? 2 : 4;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(logits), b = reinterpret_cast<uintptr_t>(d_logits);
+  const uintptr_t n = (uintptr_t)T * (uintptr_t)p.vocab * esz;
+  if (a < b + n && b < a + n) return FLCE_ERR_INVALID_ARG;  // overlapping input and output
+  if ((st = check_ws(p, workspace, workspace_bytes)) != FLCE_OK) return st;
+  float* scale = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up((size_t)T * 4, kAlign));
+  const int mb = mask ? mask_elem_bytes : 0;
+  {
+    TraceScope tr(FLCE_KERNEL_AUX, 0.0, stream);
+    hipLaunchKernelGGL(k_scale, dim3(1), dim3(kFinalizeThreads), 0, stream, labels, mask, mb, T, p.vocab,
+                       p.ignore_index, (int)p.reduction, p.num_label_tokens, grad_out, scale);
+  }
+  {
+    TraceScope tr(FLCE_KERNEL_CE_BACKWARD, 0.0, stream);
+    if (p.logits_dtype == FLCE_DTYPE_BF16)
+      hipLaunchKernelGGL(k_row_backward<bf16>, dim3((unsigned)T), dim3(kThreads), 0, stream,
+                         static_cast<const bf16*>(logits), p.vocab, labels, mask, mb, p.ignore_index, lse,
+                         (const float*)scale, static_cast<bf16*>(d_logits), device_status);
+    else
+      hipLaunchKernelGGL(k_row_backward<float>, dim3((unsigned)T), dim3(kThreads), 0, stream,
+                         static_cast<const float*>(logits), p.vocab, labels, mask, mb, p.ignore_index, lse,
+                         (const float*)scale, static_cast<float*>(d_logits), device_status);
+  }
+  return launch_status();
+}
+
+int chunked_ce_mask_labels(int64_t* labels, const void* mask, int32_t mask_elem_bytes, int64_t count,
+                           int64_t ignore_index, hipStream_t stream) {
+  if (count < 0) return FLCE_ERR_INVALID_ARG;
+  if (count == 0) return FLCE_OK;
+  if (!labels || !mask || !mask_ok(mask, mask_elem_bytes)) return FLCE_ERR_INVALID_ARG;
+  if (!aligned(labels, 8) || !aligned(mask, mask_elem_bytes)) return FLCE_ERR_UNSUPPORTED;
+  TraceScope tr(FLCE_KERNEL_AUX, 0.0, stream);
+  hipLaunchKernelGGL(k_mask_labels, dim3(grid_for(count, 256, 4096)), dim3(256), 0, stream, labels, mask,
+                     (int)mask_elem_bytes, count, ignore_index);
+  return launch_status();
+}
+
+}  // extern "C"

@@ -20,6 +20,7 @@
 
 #include "../../include/flce.h"
 #include "epilogues.hpp"
+#include "host_common.hpp"
 
 namespace flce {
 
@@ -195,12 +196,17 @@ __global__ __launch_bounds__(256) void k_round_bf16_vec(const float4* __restrict
 // Host side
 // ---------------------------------------------------------------------------
 
+// The launch tracer shared by every entry point of the library.
+namespace host {
+Tracer g_trace;
+}  // namespace host
+
 namespace {
+
+using namespace host;
 
 constexpr size_t kAlign = 256;
 
-size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Sizes derived from a validated problem.
 struct Plan {
@@ -319,70 +325,17 @@ Plan make_plan(const flce_problem_t* p, int n_cu = 256) {
 template <class T>
 T* ws_at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
 
-bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
-
 int check_workspace(const Plan& pl, void* ws, size_t bytes) {
   if (pl.total == 0) return FLCE_OK;
   if (!ws || !aligned(ws, kAlign) || bytes < pl.total) return FLCE_ERR_WORKSPACE;
   return FLCE_OK;
 }
 
-int launch_status() {
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) {
-    fprintf(stderr, "flce: HIP launch failed: %s\n", hipGetErrorString(e));
-    return FLCE_ERR_HIP;
-  }
-  return FLCE_OK;
-}
-
-// Launch tracing (flce_trace_*): (start, end) event pairs around launches.
-struct Tracer {
-  bool on = false;
-  int cap = 0;
-  int n = 0;
-  std::vector<hipEvent_t> ev;
-  std::vector<int> kind;
-  std::vector<double> flops;
-  void release() {
-    for (hipEvent_t e : ev) hipEventDestroy(e);
-    ev.clear();
-    kind.clear();
-    flops.clear();
-    cap = n = 0;
-    on = false;
-  }
-};
-Tracer g_trace;
-
-// Brackets one launch with trace events when a trace is running.
-struct TraceScope {
-  int slot = -1;
-  hipStream_t s;
-  TraceScope(int kind, double flops, hipStream_t stream) : s(stream) {
-    if (!g_trace.on || g_trace.n >= g_trace.cap) return;
-    slot = g_trace.n++;
-    g_trace.kind[slot] = kind;
-    g_trace.flops[slot] = flops;
-    hipEventRecord(g_trace.ev[2 * slot], s);
-  }
-  ~TraceScope() {
-    if (slot >= 0) hipEventRecord(g_trace.ev[2 * slot + 1], s);
-  }
-};
-
 // K steps of BK for a K extent, padded to whole groups of NST stages (the
 // operands are zero, or multiplied by zero, in the padding).
 int k_steps_for(int64_t K) {
   const int64_t group = (int64_t)gemm::NST * gemm::BK;
   return (int)(ceil_div(K, group) * gemm::NST);
-}
-
-unsigned grid_for(int64_t n, int64_t per_block, int64_t cap) {
-  int64_t g = ceil_div(n, per_block);
-  if (g < 1) g = 1;
-  if (g > cap) g = cap;
-  return (unsigned)g;
 }
 
 void zero_fill(void* p, int64_t bytes, hipStream_t s) {

@@ -18,9 +18,14 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared_functions():
-    src = open(os.path.join(ROOT, "include", "flce.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(flce_[a-z0-9_]+)\s*\(", src)))
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for h in sorted(os.listdir(inc)):
+        if not h.endswith(".h"):
+            continue
+        src = re.sub(r"/\*.*?\*/", "", open(os.path.join(inc, h)).read(), flags=re.S)
+        names |= set(re.findall(r"\b((?:flce|chunked_ce)_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_header_declares_the_abi():
@@ -143,3 +148,81 @@ def test_python_binding_argument_errors():
         make_problem(4, 128, 10, reduction="none")
     with pytest.raises(ValueError):
         make_problem(4, 128, 10, num_label_tokens=-3)
+
+
+# ---------------------------------------------------------------------------
+# Cross-entropy over given logits (include/chunked_ce.h)
+# ---------------------------------------------------------------------------
+
+
+def _ce_ws(problem):
+    out = ctypes.c_size_t(0)
+    return _lib.load().chunked_ce_workspace_size(ctypes.byref(problem), ctypes.byref(out)), out.value
+
+
+def test_chunked_ce_workspace_is_per_position():
+    from lm_head_cross_amd.chunked_ce import make_ce_problem
+    code, ws = _ce_ws(make_ce_problem(4096, 128256))
+    assert code == _lib.FLCE_OK and 4096 * 4 <= ws < 4096 * 16
+    code, ws = _ce_ws(make_ce_problem(0, 10))
+    assert code == _lib.FLCE_OK and ws == 0
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(vocab=0), _lib.FLCE_ERR_INVALID_ARG),
+    (dict(num_tokens=-1), _lib.FLCE_ERR_INVALID_ARG),
+    (dict(chunk_len=0), _lib.FLCE_ERR_INVALID_ARG),
+    (dict(reduction=7), _lib.FLCE_ERR_INVALID_ARG),
+    (dict(num_label_tokens=0), _lib.FLCE_ERR_INVALID_ARG),
+    (dict(logits_dtype=5), _lib.FLCE_ERR_UNSUPPORTED),
+])
+def test_chunked_ce_invalid_problem_rejected(kw, expect):
+    from lm_head_cross_amd.chunked_ce import make_ce_problem
+    p = make_ce_problem(8, 100)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    assert _ce_ws(p)[0] == expect
+    lib = _lib.load()
+    f = ctypes.c_void_p(1 << 20)
+    assert lib.chunked_ce_forward(ctypes.byref(p), f, f, None, 0, f, f, None, None, f, 1 << 20, None) == expect
+    assert lib.chunked_ce_backward(ctypes.byref(p), f, f, None, 0, f, f, f, None, f, 1 << 20, None) == expect
+
+
+def test_chunked_ce_pointer_checks():
+    from lm_head_cross_amd.chunked_ce import make_ce_problem
+    lib = _lib.load()
+    p = make_ce_problem(64, 1000)
+    code, need = _ce_ws(p)
+    P = ctypes.byref(p)
+    V = ctypes.c_void_p
+    a = 1 << 24
+    # required pointers
+    assert lib.chunked_ce_forward(P, None, V(a), None, 0, V(a), V(a), None, None, V(a), need, None) == 1
+    assert lib.chunked_ce_forward(P, V(a), V(a), None, 0, None, V(a), None, None, V(a), need, None) == 1
+    assert lib.chunked_ce_backward(P, V(a), V(a), None, 0, V(a), None, V(a), None, V(a), need, None) == 1
+    # mask element size
+    assert lib.chunked_ce_forward(P, V(a), V(a), V(a), 3, V(a), V(a), None, None, V(a), need, None) == 1
+    # alignment: logits, labels, mask elements
+    assert lib.chunked_ce_forward(P, V(a + 2), V(a), None, 0, V(a), V(a), None, None, V(a), need, None) == 2
+    assert lib.chunked_ce_forward(P, V(a), V(a + 4), None, 0, V(a), V(a), None, None, V(a), need, None) == 2
+    assert lib.chunked_ce_forward(P, V(a), V(a), V(a + 2), 4, V(a), V(a), None, None, V(a), need, None) == 2
+    # workspace
+    assert lib.chunked_ce_forward(P, V(a), V(a), None, 0, V(a), V(a), None, None, None, need, None) == 3
+    assert lib.chunked_ce_forward(P, V(a), V(a), None, 0, V(a), V(a), None, None, V(a), need - 1, None) == 3
+    # gradient may not overlap the logits
+    assert lib.chunked_ce_backward(P, V(a), V(a), None, 0, V(a), V(a), V(a + 1024), None, V(a), need, None) == 1
+    # in-place label rewrite
+    assert lib.chunked_ce_mask_labels(V(a), None, 1, 8, -100, None) == 1
+    assert lib.chunked_ce_mask_labels(V(a), V(a), 1, -1, -100, None) == 1
+    assert lib.chunked_ce_mask_labels(V(a + 4), V(a), 1, 8, -100, None) == 2
+    assert lib.chunked_ce_mask_labels(None, None, 1, 0, -100, None) == 0
+
+
+def test_chunked_ce_module_arguments():
+    import lm_head_cross_amd as L
+    with pytest.raises(ValueError):
+        L.ChunkedCrossEntropy(chunk_len=0)
+    with pytest.raises(ValueError):
+        L.ChunkedCrossEntropy(reduction="none")
+    with pytest.raises(NotImplementedError):
+        L.make_ce_problem(4, 10, dtype=__import__("torch").float16)

@@ -1,0 +1,261 @@
+"""GPU parity of the cross-entropy over given logits (include/chunked_ce.h)
+against the CPU oracle.
+
+Small shapes are compared element by element over every output, including
+rows that are not 16-byte multiples (scalar head and tail paths) and every
+mask element size.  The full-size workloads are checked on every position's
+loss and lse (the oracle's lse of each row from the same logits), the total
+loss, and the gradient on a seeded subset of >= 512 positions; rows of
+ignored positions must be exactly zero.
+
+Tolerances are those of the fused path: per-position loss 2e-3 absolute,
+total loss 1e-4 relative, gradient rel-L2 1e-2 (a bf16 gradient carries
+bf16 rounding, about 2e-3 rms).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import lm_head_cross_amd as L
+import oracle
+from tests.gpu_common import TOL_GRAD_REL_L2, TOL_TOKEN_ABS, TOL_TOTAL_REL, rel_l2, say
+from workloads import LOGIT_WORKLOADS, LogitsWorkload, make_logit_inputs, sample_logit_rows
+
+pytestmark = pytest.mark.gpu
+
+D = torch.device("cuda:0")
+
+
+def _problem(inp):
+    z = inp["logits"]
+    return L.make_ce_problem(z.shape[0], z.shape[1], z.dtype, inp["ignore_index"], inp["reduction"],
+                             inp["num_label_tokens"])
+
+
+def _run(inp, grad_out=1.0, rows=None):
+    """Forward + backward through the C ABI; CPU results."""
+    z = inp["logits"].to(D)
+    y = inp["labels"].to(D)
+    m = None if inp.get("mask") is None else inp["mask"].to(D)
+    p = _problem(inp)
+    T = z.shape[0]
+    loss = torch.empty((), device=D)
+    lse = torch.empty(T, device=D)
+    tl = torch.empty(T, device=D)
+    st = torch.zeros((), dtype=torch.int32, device=D)
+    L.chunked_ce_forward(p, z, y, loss, lse, mask=m, token_loss=tl, device_status=st)
+    g = torch.tensor(grad_out, device=D)
+    dz = torch.empty_like(z)
+    L.chunked_ce_backward(p, z, y, lse, g, dz, mask=m, device_status=st)
+    torch.cuda.synchronize()
+    out = {"loss": loss.item(), "lse": lse.cpu(), "token_loss": tl.cpu(), "status": st.item()}
+    if rows is None:
+        out["dz"] = dz.float().cpu()
+    else:
+        out["dz_rows"] = dz[torch.from_numpy(rows).to(D)].float().cpu()
+        out["dz_dev"] = dz
+    return out
+
+
+def _ref_problem(inp):
+    return oracle.CEProblem(ignore_index=inp["ignore_index"], reduction=inp["reduction"],
+                            num_label_tokens=inp["num_label_tokens"])
+
+
+def _check_full(inp, res, grad_out=1.0, label=""):
+    z = oracle.to_f64(inp["logits"].cpu())
+    y = inp["labels"].cpu().numpy()
+    m = None if inp.get("mask") is None else inp["mask"].cpu().numpy()
+    p = _ref_problem(inp)
+    ref = oracle.ce_forward(z, y, p, mask=m)
+    counted = ~np.isnan(ref.lse)
+    tl_err = np.abs(res["token_loss"].double().numpy() - ref.token_loss).max()
+    lse_err = np.abs(res["lse"].double().numpy()[counted] - ref.lse[counted]).max() if counted.any() else 0.0
+    say(f"  {label}: loss gpu={res['loss']:.9g} ref={ref.loss:.9g}  max|dl|={tl_err:.3g} max|dlse|={lse_err:.3g}")
+    assert tl_err <= TOL_TOKEN_ABS and lse_err <= TOL_TOKEN_ABS
+    assert np.all(res["lse"].numpy()[~counted] == 0)
+    if math.isnan(ref.loss):
+        assert math.isnan(res["loss"])
+    else:
+        assert abs(res["loss"] - ref.loss) <= TOL_TOTAL_REL * max(abs(ref.loss), 1e-30)
+    gref = oracle.ce_backward(z, y, p, mask=m, grad_out=grad_out)
+    e = rel_l2(res["dz"].double().numpy(), gref)
+    say(f"  {label}: grad rel-L2 {e:.3g}")
+    assert e <= TOL_GRAD_REL_L2
+    assert torch.all(res["dz"][torch.from_numpy(~counted)] == 0)
+
+
+def _small(key, **kw):
+    base = dict(name=key, std=2.0)
+    base.update(kw)
+    return LogitsWorkload(key=key, **base)
+
+
+SMALL = {
+    "ce1_fp32_unaligned_rows": LOGIT_WORKLOADS["ce1"],
+    "bf16_odd_vocab": _small("ce101", T=300, V=4099, dtype="bf16", ignore_frac=0.05),
+    "fp32_masked_mean_count": _small("ce102", T=257, V=3001, dtype="fp32", ignore_frac=0.2, reduction="mean",
+                                     normalise_by_count=True, use_mask=True),
+    "bf16_runs_mean_peaked": _small("ce103", T=2000, V=2048, dtype="bf16", std=3.0, ignore="runs",
+                                    reduction="mean", peak=12.0),
+    "bf16_one_column_short_rows": _small("ce104", T=100, V=7, dtype="bf16", ignore_frac=0.1),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_full_parity(name):
+    w = SMALL[name]
+    say(f"case {name}: T={w.T} V={w.V} {w.dtype} {w.reduction}")
+    inp = make_logit_inputs(w)
+    res = _run(inp)
+    assert res["status"] == 0
+    _check_full(inp, res, label=name)
+
+
+def test_grad_out_scaling():
+    inp = make_logit_inputs(SMALL["fp32_masked_mean_count"])
+    _check_full(inp, _run(inp, grad_out=-2.5), grad_out=-2.5, label="grad_out=-2.5")
+
+
+@pytest.mark.parametrize("mdtype", [torch.bool, torch.uint8, torch.int8, torch.int16, torch.int32, torch.int64,
+                                    torch.float32])
+def test_mask_element_types(mdtype):
+    inp = make_logit_inputs(SMALL["fp32_masked_mean_count"])
+    inp = dict(inp)
+    inp["mask"] = (inp["mask"] != 0).to(mdtype) * (3 if mdtype not in (torch.bool,) else 1)
+    if mdtype == torch.bool:
+        inp["mask"] = inp["mask"].bool()
+    _check_full(inp, _run(inp), label=f"mask {mdtype}")
+
+
+def test_deterministic_repeat():
+    inp = make_logit_inputs(SMALL["bf16_runs_mean_peaked"])
+    a, b = _run(inp), _run(inp)
+    assert a["loss"] == b["loss"]
+    for k in ("lse", "token_loss", "dz"):
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_ignored_rows_never_read():
+    """NaN in the rows of ignored positions changes nothing."""
+    inp = make_logit_inputs(SMALL["bf16_odd_vocab"])
+    a = _run(inp)
+    poisoned = dict(inp)
+    z = inp["logits"].clone()
+    z[inp["labels"] == -100] = float("nan")
+    poisoned["logits"] = z
+    b = _run(poisoned)
+    assert a["loss"] == b["loss"]
+    for k in ("lse", "token_loss", "dz"):
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_bad_labels_flagged_and_skipped():
+    inp = make_logit_inputs(SMALL["bf16_odd_vocab"])
+    y = inp["labels"].clone()
+    bad = dict(inp)
+    yb = y.clone()
+    yb[[1, 7]] = torch.tensor([5000, -5])
+    bad["labels"] = yb
+    res = _run(bad)
+    assert res["status"] == 1
+    ref = dict(inp)
+    yr = y.clone()
+    yr[[1, 7]] = -100
+    ref["labels"] = yr
+    _check_full(ref, res, label="bad labels as ignored")
+
+
+@pytest.mark.parametrize("reduction", ["sum", "mean"])
+def test_all_positions_ignored(reduction):
+    inp = dict(make_logit_inputs("ce1"))
+    inp["labels"] = torch.full_like(inp["labels"], -100)
+    inp["reduction"] = reduction
+    res = _run(inp)
+    assert (res["loss"] == 0.0) if reduction == "sum" else math.isnan(res["loss"])
+    assert torch.all(res["dz"] == 0) and torch.all(res["lse"] == 0)
+
+
+def test_empty_batch():
+    p = L.make_ce_problem(0, 100, torch.float32, reduction="mean")
+    z = torch.empty((0, 100), device=D)
+    y = torch.empty(0, dtype=torch.int64, device=D)
+    loss = torch.zeros((), device=D)
+    L.chunked_ce_forward(p, z, y, loss, torch.empty(0, device=D))
+    L.chunked_ce_backward(p, z, y, torch.empty(0, device=D), torch.ones((), device=D), torch.empty_like(z))
+    torch.cuda.synchronize()
+    assert math.isnan(loss.item())
+
+
+def test_module_mask_rewrites_labels_and_autograd():
+    """ChunkedCrossEntropy.forward with a mask: the masked positions' labels
+    become ignore_index in the caller's tensor (the page's documented side
+    effect), and loss.backward() gives the oracle's gradient."""
+    inp = make_logit_inputs(SMALL["fp32_masked_mean_count"])
+    T, V = inp["logits"].shape
+    z = inp["logits"].to(D).reshape(1, T, V).clone().requires_grad_(True)
+    y = inp["labels"].to(D).reshape(1, T).clone()
+    m = inp["mask"].to(D).reshape(1, T)
+    mod = L.ChunkedCrossEntropy(chunk_len=16, reduction="mean")
+    loss = mod(z, y, mask=m, num_label_tokens=inp["num_label_tokens"])
+    loss.backward()
+    torch.cuda.synchronize()
+    y_ref = np.where(inp["mask"].numpy() != 0, inp["labels"].numpy(), -100)
+    assert np.array_equal(y.cpu().numpy().reshape(-1), y_ref)
+    zc = oracle.to_f64(inp["logits"])
+    p = oracle.CEProblem(reduction="mean", num_label_tokens=inp["num_label_tokens"])
+    ref = oracle.ce_forward(zc, y_ref, p)
+    assert abs(loss.item() - ref.loss) <= TOL_TOTAL_REL * abs(ref.loss)
+    e = rel_l2(z.grad.reshape(T, V).double().cpu().numpy(), oracle.ce_backward(zc, y_ref, p))
+    assert e <= TOL_GRAD_REL_L2
+    # compute_cross_entropy is the same sum-reduced loss
+    s = L.compute_cross_entropy(inp["logits"].to(D), torch.from_numpy(y_ref).to(D))
+    assert abs(s.item() - oracle.ce_forward(zc, y_ref, oracle.CEProblem()).loss) <= TOL_TOTAL_REL * abs(s.item())
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads, sampled gradient checks
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("key", ["ce2", "ce3", "ce4"])
+def test_workload_full_size(key):
+    w = LOGIT_WORKLOADS[key]
+    say(f"workload {key}: {w.name}")
+    inp = make_logit_inputs(w, device="cuda:0")
+    y = inp["labels"].cpu().numpy()
+    m = None if inp["mask"] is None else inp["mask"].cpu().numpy()
+    yeff = oracle.apply_mask(y, m, -100)
+    counted = yeff != -100
+    rows = sample_logit_rows(w, counted)
+    res = _run(inp, rows=rows)
+    assert res["status"] == 0
+    assert torch.all(res["dz_dev"][torch.from_numpy(~counted).to(D)] == 0)
+    del res["dz_dev"]
+    # every position's lse from the same logits, in row blocks
+    zc = inp["logits"].cpu()
+    lse_ref = np.full(w.T, np.nan)
+    idx = np.nonzero(counted)[0]
+    for b in range(0, len(idx), 512):
+        r = idx[b:b + 512]
+        lse_ref[r] = oracle.ce_lse(oracle.to_f64(zc[torch.from_numpy(r)]))
+    zy = oracle.to_f64(zc[torch.from_numpy(idx), torch.from_numpy(yeff[idx])])
+    tl_ref = np.zeros(w.T)
+    tl_ref[idx] = lse_ref[idx] - zy
+    D_ = float(inp["num_label_tokens"]) if inp["num_label_tokens"] else (len(idx) if w.reduction == "mean" else 1.0)
+    ref_loss = float(np.sum(np.sort(tl_ref))) / D_
+    tl_err = np.abs(res["token_loss"].double().numpy() - tl_ref).max()
+    lse_err = np.abs(res["lse"].double().numpy()[counted] - lse_ref[counted]).max()
+    say(f"  loss gpu={res['loss']:.9g} ref={ref_loss:.9g} max|dl|={tl_err:.3g} max|dlse|={lse_err:.3g}")
+    assert tl_err <= TOL_TOKEN_ABS and lse_err <= TOL_TOKEN_ABS
+    assert abs(res["loss"] - ref_loss) <= TOL_TOTAL_REL * abs(ref_loss)
+    # gradient rows
+    rc = rows[counted[rows]]
+    sel = np.isin(rows, rc)
+    g_ref = oracle.ce_rows(oracle.to_f64(zc[torch.from_numpy(rc)]), yeff[rc], lse_ref[rc], 1.0 / D_)
+    e = rel_l2(res["dz_rows"][torch.from_numpy(sel)].double().numpy(), g_ref)
+    say(f"  grad rel-L2 over {len(rc)} counted rows = {e:.3g}")
+    assert e <= TOL_GRAD_REL_L2
+    assert torch.all(res["dz_rows"][torch.from_numpy(~sel)] == 0)

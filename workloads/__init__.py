@@ -24,6 +24,19 @@ Workloads (T tokens, H hidden, V head rows of which Vu are usable):
    70% the row's argmax logit and 30% uniform, 2% ignored, c=30.
 
 The N(0, s) notation takes s as the standard deviation.
+
+Cross-entropy over given logits (LOGIT_WORKLOADS; the chunked CE page gives
+no shapes, so these take the shapes above, with the logits drawn directly):
+
+ce1. tiny: T=64, V=1000, fp32 logits ~N(0,1), 10% ignored (rows of 4000 B,
+     not 16-byte multiples).
+ce2. llama3-8b head: T=4096, V=128256, bf16 logits ~N(0,2), 5% ignored.
+ce3. masked fp32: T=2048, V=256000, fp32 logits ~N(0,2); 5% of positions
+     dropped by an int32 mask whose labels there are out of range; mean,
+     divided by the supplied count of kept positions.
+ce4. packed peaked batch: T=16384, V=152064, bf16 logits ~N(0,3) with the
+     label's logit raised by 12 at 70% of positions; half the positions
+     ignored in runs of 64..512; mean over the counted positions.
 """
 from __future__ import annotations
 
@@ -222,3 +235,98 @@ def sample_rows(key_or_workload, labels: np.ndarray, n_tokens=512, n_vocab=512, 
         voc.add(int(rng.integers(0, Vu)))
     voc = np.array(sorted(voc), dtype=np.int64)
     return tok, voc
+
+
+# ---------------------------------------------------------------------------
+# Cross-entropy over given logits
+# ---------------------------------------------------------------------------
+
+
+@dataclasses.dataclass(frozen=True)
+class LogitsWorkload:
+    """Shape and value distributions of one logits-input workload."""
+
+    key: str
+    name: str
+    T: int
+    V: int
+    dtype: str             # "bf16" | "fp32"
+    std: float
+    ignore: str = "uniform"
+    ignore_frac: float = 0.0
+    reduction: str = "sum"
+    normalise_by_count: bool = False
+    use_mask: bool = False  # drop positions through an int32 mask instead of ignore_index
+    peak: float = 0.0       # added to the label's logit at 70% of positions
+
+    @property
+    def seed(self) -> int:
+        return 2000 + int(self.key[2:])
+
+
+LOGIT_WORKLOADS = {
+    "ce1": LogitsWorkload("ce1", "tiny logits T=64 V=1000 fp32", 64, 1000, "fp32", 1.0, ignore_frac=0.10),
+    "ce2": LogitsWorkload("ce2", "llama3-8b logits T=4096 V=128256 bf16", 4096, 128256, "bf16", 2.0,
+                          ignore_frac=0.05),
+    "ce3": LogitsWorkload("ce3", "masked fp32 logits T=2048 V=256000", 2048, 256000, "fp32", 2.0, ignore_frac=0.05,
+                          reduction="mean", normalise_by_count=True, use_mask=True),
+    "ce4": LogitsWorkload("ce4", "packed peaked logits T=16384 V=152064 bf16", 16384, 152064, "bf16", 3.0,
+                          ignore="runs", reduction="mean", peak=12.0),
+}
+
+
+def make_logit_inputs(key_or_workload, device="cpu"):
+    """Draw one logits-input workload.
+
+    Returns ``logits`` ([T,V], bf16 or fp32), ``labels`` (int64 [T]), ``mask``
+    (int32 [T] or None) and the loss knobs, on ``device``.  With a mask, the
+    dropped positions carry labels outside [0, V) that the mask must hide.
+    """
+    w = key_or_workload if isinstance(key_or_workload, LogitsWorkload) else LOGIT_WORKLOADS[key_or_workload]
+    sz, sl = np.random.SeedSequence(w.seed).spawn(2)
+    Z = _normal_f32((w.T, w.V), sz, w.std)
+    rng = np.random.Generator(np.random.PCG64(sl))
+    shape_only = Workload(key=0, name=w.name, T=w.T, H=1, V=w.V, Vu=w.V, x_std=1.0, w_std=1.0, ignore=w.ignore,
+                          ignore_frac=w.ignore_frac)
+    dropped = _ignore_mask(shape_only, rng)
+    labels = rng.integers(0, w.V, size=w.T, dtype=np.int64)
+    if w.peak:
+        boost = np.nonzero(rng.random(w.T) < 0.7)[0]
+        Z[boost, labels[boost]] += np.float32(w.peak)
+    mask = None
+    if w.use_mask:
+        mask = (~dropped).astype(np.int32)
+        labels[dropped] = w.V + rng.integers(0, 1000, size=int(dropped.sum()))
+    else:
+        labels[dropped] = IGNORE_INDEX
+    n_valid = int((~dropped).sum())
+    logits = torch.from_numpy(Z)
+    if w.dtype == "bf16":
+        logits = logits.to(torch.bfloat16)
+    del Z
+    dev = torch.device(device)
+    return {
+        "workload": w,
+        "logits": logits.to(dev),
+        "labels": torch.from_numpy(labels).to(dev),
+        "mask": None if mask is None else torch.from_numpy(mask).to(dev),
+        "ignore_index": IGNORE_INDEX,
+        "reduction": w.reduction,
+        "num_label_tokens": n_valid if w.normalise_by_count else None,
+        "n_valid": n_valid,
+    }
+
+
+def sample_logit_rows(key_or_workload, counted: np.ndarray, n_rows=512, n_ignored=64):
+    """Seeded positions for sampled gradient checks: 0 and T-1, at least
+    ``n_rows`` counted positions (all if fewer), and up to ``n_ignored``
+    ignored ones (whose gradient rows must be zero)."""
+    w = key_or_workload if isinstance(key_or_workload, LogitsWorkload) else LOGIT_WORKLOADS[key_or_workload]
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(w.seed + 7)))
+    on = np.nonzero(counted)[0]
+    off = np.nonzero(~counted)[0]
+    rows = {0, w.T - 1}
+    rows.update(int(v) for v in rng.choice(on, size=min(n_rows, len(on)), replace=False))
+    if len(off):
+        rows.update(int(v) for v in rng.choice(off, size=min(n_ignored, len(off)), replace=False))
+    return np.array(sorted(rows), dtype=np.int64)
