@@ -346,6 +346,15 @@ def bench_chunked_ce(args):
     step_bytes = alg["ce_forward"] + alg["ce_backward"]
     log(f"step {ms:.3f} ms  {T / (ms * 1e-3):,.0f} tokens/s  {step_bytes / (ms * 1e-3) / 1e9:.0f} GB/s "
         f"algorithmic ({step_bytes / (ms * 1e-3) / 8e12 * 100:.1f}% of HBM peak)  loss={loss.item():.6g}")
+    if args.calibration_copy_mib > 0:
+        n = args.calibration_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {n} bytes read, {n} bytes written")
+        del src, dst
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_ce(inp, 256)
