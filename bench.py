@@ -99,6 +99,9 @@ def main():
                     help="flce: fused linear cross-entropy (the default workload); chunked_ce: cross-entropy "
                          "over given logits")
     ap.add_argument("--ce-workload", default="ce2", help="logits-input workload for --path chunked_ce")
+    ap.add_argument("--fp32-head-direct", action="store_true",
+                    help="hand an fp32 head to the calls as fp32 (each call rounds and stages it, inside the "
+                         "timed region) instead of rounding it once before timing")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -120,11 +123,13 @@ def main():
     inp = make_inputs(w, device="cuda:0", argmax_device="cuda:0")
     X, y = inp["hidden"], inp["labels"]
     W = inp["weight"]
-    if W.dtype == torch.float32:
+    direct = args.fp32_head_direct and W.dtype == torch.float32
+    if W.dtype == torch.float32 and not direct:
         W = L.flce_round_to_bf16(W)
     T, H, V, Vu = w.T, w.H, w.V, w.Vu
     Tv = inp["n_valid"]
-    p = L.make_problem(T, H, V, Vu, w.softcap, inp["ignore_index"], w.reduction, inp["num_label_tokens"])
+    p = L.make_problem(T, H, V, Vu, w.softcap, inp["ignore_index"], w.reduction, inp["num_label_tokens"],
+                       W.dtype)
     ws = L.alloc_workspace(p, dev)
     loss = torch.empty((), dtype=torch.float32, device=dev)
     lse = torch.empty(T, dtype=torch.float32, device=dev)
@@ -239,7 +244,7 @@ def main():
         "config": {
             "workload": w.name,
             "tokens": T, "hidden": H, "vocab": V, "unpadded_vocab": Vu, "valid_tokens": Tv,
-            "softcap": w.softcap, "reduction": w.reduction,
+            "softcap": w.softcap, "reduction": w.reduction, "head": str(W.dtype).replace("torch.", ""),
             "num_label_tokens": inp["num_label_tokens"],
             "credited_tflop_per_step": round(credited / 1e12, 3),
             "model_tflop_per_step": round(6.0 * Tv * Vu * H / 1e12, 3),

@@ -92,8 +92,12 @@ typedef enum flce_dtype {
  * num_label_tokens  > 0: divide the summed loss by this count whatever the
  *                   reduction (linear_ce page, forward argument
  *                   num_label_tokens); < 0: not given.  0 is invalid.
- * weight_dtype      FLCE_DTYPE_BF16 (the only head dtype accepted here; an
- *                   fp32 head is rounded to bf16 by the caller).
+ * weight_dtype      FLCE_DTYPE_BF16, or FLCE_DTYPE_FP32 for an fp32 head that
+ *                   each call rounds to bf16 itself (Inkling2 page, class
+ *                   description: an FP32 head is rounded to BF16, the cast
+ *                   FSDP applies).  The rounded copy of rows < Vu is staged
+ *                   in the workspace, which grows by Vu*H*2 bytes; rows >= Vu
+ *                   are never read.
  */
 typedef struct flce_problem {
   int64_t num_tokens;
@@ -125,7 +129,8 @@ int flce_workspace_size(const flce_problem_t* problem, size_t* bytes);
  * Forward pass.
  *
  * hidden       bf16 [T, H], 16-byte aligned.
- * weight       bf16 [V, H], 16-byte aligned; rows >= Vu are never read.
+ * weight       [V, H] in weight_dtype (bf16 or fp32), 16-byte aligned; rows
+ *              >= Vu are never read.
  * labels       int64 [T].
  * loss         fp32 scalar (device): the reduced loss; NaN for MEAN with no
  *              valid position and no num_label_tokens (0/0, as PyTorch).

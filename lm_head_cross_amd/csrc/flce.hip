@@ -219,6 +219,7 @@ struct Plan {
   int64_t nchunks;
   // workspace byte offsets
   size_t off_meta, off_valid, off_yc, off_label, off_scale, off_bsum, off_xc;
+  size_t off_wst;       // bf16 staging of an fp32 head's rows < Vu (0 bytes for a bf16 head)
   size_t off_part;      // forward region
   size_t off_g, off_hacc;  // backward region
   size_t total;
@@ -231,7 +232,7 @@ int validate(const flce_problem_t* p) {
   if (!(p->softcap >= 0.0f) || isinf(p->softcap)) return FLCE_ERR_INVALID_ARG;
   if (p->reduction != FLCE_REDUCTION_SUM && p->reduction != FLCE_REDUCTION_MEAN) return FLCE_ERR_INVALID_ARG;
   if (p->num_label_tokens == 0) return FLCE_ERR_INVALID_ARG;
-  if (p->weight_dtype != FLCE_DTYPE_BF16) return FLCE_ERR_UNSUPPORTED;
+  if (p->weight_dtype != FLCE_DTYPE_BF16 && p->weight_dtype != FLCE_DTYPE_FP32) return FLCE_ERR_UNSUPPORTED;
   if (p->hidden % 128 != 0) return FLCE_ERR_UNSUPPORTED;
   // 32-bit token / row / column indices inside the kernels.
   if (p->num_tokens > (int64_t(1) << 30) || p->vocab > (int64_t(1) << 30) || p->hidden > (int64_t(1) << 20))
@@ -310,6 +311,8 @@ Plan make_plan(const flce_problem_t* p, int n_cu = 256) {
   pl.off_scale = take(16);
   pl.off_bsum = take(pl.Tvp / kCombineTokens * 8);
   pl.off_xc = take(pl.Tvp * pl.H * 2);
+  // An fp32 head: the bf16 copy of its usable rows, staged here by each call.
+  pl.off_wst = take(p->weight_dtype == FLCE_DTYPE_FP32 ? pl.Vu * pl.H * 2 : 0);
   const size_t common = o;
   pl.off_part = take(pl.tiles_v * pl.Tvp * 8);
   const size_t fwd_end = o;
@@ -343,6 +346,22 @@ void zero_fill(void* p, int64_t bytes, hipStream_t s) {
   TraceScope tr(FLCE_KERNEL_AUX, 0.0, s);
   const int64_t n16 = bytes / 16;
   hipLaunchKernelGGL(k_zero, dim3(grid_for(n16, 256, 8192)), dim3(256), 0, s, (uint4*)p, n16);
+}
+
+// The bf16 head the kernels read: the caller's for a bf16 head; for an fp32
+// head its rows < Vu rounded to nearest even into the workspace ("nemo_
+// automodel.components.models.inkling2.loss", class description: an fp32
+// head is rounded to bf16 with the cast FSDP applies).  Rows >= Vu are never
+// read.
+const bf16* staged_head(const Plan& pl, const flce_problem_t& p, const void* weight, void* workspace,
+                        hipStream_t stream) {
+  if (p.weight_dtype == FLCE_DTYPE_BF16) return static_cast<const bf16*>(weight);
+  bf16* wst = ws_at<bf16>(workspace, pl.off_wst);
+  const int64_t n4 = pl.Vu * pl.H / 4;  // H is a multiple of 128
+  TraceScope tr(FLCE_KERNEL_AUX, 0.0, stream);
+  hipLaunchKernelGGL(k_round_bf16_vec, dim3(grid_for(n4, 256, 16384)), dim3(256), 0, stream,
+                     static_cast<const float4*>(weight), reinterpret_cast<bf16x4*>(wst), n4);
+  return wst;
 }
 
 void launch_compact_gather(const Plan& pl, const flce_problem_t& p, const int64_t* labels, const void* hidden,
@@ -432,9 +451,10 @@ int flce_forward(const flce_problem_t* problem, const void* hidden, const void* 
   float2* part = ws_at<float2>(workspace, pl.off_part);
   const int* tv = &meta->n_valid;
 
+  const bf16* Wb = staged_head(pl, p, weight, workspace, stream);
   launch_compact_gather(pl, p, labels, hidden, meta, valid_idx, yc, device_status, lse, token_loss, xc, stream);
   {
-    gemm::Operand A{(const bf16*)weight, pl.H, (int)pl.Vu - 1, 0};
+    gemm::Operand A{Wb, pl.H, (int)pl.Vu - 1, 0};
     gemm::Operand B{xc, pl.H, (int)pl.Tvp - 1, 0};
     gemm::Schedule sch{(int)pl.tiles_v, (int)pl.tiles_t, k_steps_for(pl.H), tv, 2};
     const dim3 grid(pl.tiles_v * pl.tiles_t);
@@ -491,7 +511,7 @@ int flce_backward(const flce_problem_t* problem, const void* hidden, const void*
   bf16* G = ws_at<bf16>(workspace, pl.off_g);
   float* hacc = ws_at<float>(workspace, pl.off_hacc);
   const int* tv = &meta->n_valid;
-  const bf16* W = (const bf16*)weight;
+  const bf16* W = staged_head(pl, p, weight, workspace, stream);
 
   launch_compact_gather(pl, p, labels, hidden, meta, valid_idx, yc, device_status, nullptr, nullptr, xc, stream);
   {

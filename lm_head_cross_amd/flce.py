@@ -36,10 +36,17 @@ def _raise_for(code: int, what: str) -> None:
     raise FlceError(msg)
 
 
+_WEIGHT_DTYPES = {torch.bfloat16: _lib.FLCE_DTYPE_BF16, torch.float32: _lib.FLCE_DTYPE_FP32}
+
+
 def make_problem(num_tokens: int, hidden: int, vocab: int, unpadded_vocab: int | None = None,
                  softcap: float = 0.0, ignore_index: int = -100, reduction: str = "sum",
-                 num_label_tokens: int | None = None) -> _lib.Problem:
-    """Fill an ``flce_problem_t``; value checks are the library's."""
+                 num_label_tokens: int | None = None, weight_dtype=torch.bfloat16) -> _lib.Problem:
+    """Fill an ``flce_problem_t``; value checks are the library's.  With
+    ``weight_dtype=torch.float32`` the calls take the fp32 head and round its
+    usable rows to bf16 themselves."""
+    if weight_dtype not in _WEIGHT_DTYPES:
+        raise NotImplementedError(f"the head must be bfloat16 or float32, got {weight_dtype}")
     if reduction not in _REDUCTIONS:
         raise ValueError(f"reduction must be one of {sorted(_REDUCTIONS)}, got {reduction!r}")
     if num_label_tokens is not None and int(num_label_tokens) < 0:
@@ -49,7 +56,7 @@ def make_problem(num_tokens: int, hidden: int, vocab: int, unpadded_vocab: int |
         unpadded_vocab=int(vocab if unpadded_vocab is None else unpadded_vocab),
         softcap=float(softcap), reduction=_REDUCTIONS[reduction], ignore_index=int(ignore_index),
         num_label_tokens=-1 if num_label_tokens is None else int(num_label_tokens),
-        weight_dtype=_lib.FLCE_DTYPE_BF16)
+        weight_dtype=_WEIGHT_DTYPES[weight_dtype])
 
 
 def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
@@ -74,6 +81,10 @@ def _need(t, name, dtype, shape, device):
         raise ValueError(f"{name} must be on {device}, got {t.device}")
 
 
+def _weight_dtype(problem):
+    return {v: k for k, v in _WEIGHT_DTYPES.items()}[problem.weight_dtype]
+
+
 def flce_workspace_size(problem: _lib.Problem) -> int:
     """Workspace bytes ``flce_forward`` / ``flce_backward`` need."""
     out = ctypes.c_size_t(0)
@@ -91,7 +102,7 @@ def flce_forward(problem, hidden, weight, labels, loss, lse, token_loss=None, de
     """Enqueue the forward pass; see include/flce.h for the contract."""
     T, H, V = problem.num_tokens, problem.hidden, problem.vocab
     dev = weight.device
-    _need(weight, "weight", torch.bfloat16, (V, H), dev)
+    _need(weight, "weight", _weight_dtype(problem), (V, H), dev)
     _need(hidden, "hidden", torch.bfloat16, (T, H), dev)
     _need(labels, "labels", torch.int64, (T,), dev)
     _need(loss, "loss", torch.float32, (), dev)
@@ -113,7 +124,7 @@ def flce_backward(problem, hidden, weight, labels, lse, grad_out, d_hidden, d_we
     """Enqueue the backward pass; see include/flce.h for the contract."""
     T, H, V = problem.num_tokens, problem.hidden, problem.vocab
     dev = weight.device
-    _need(weight, "weight", torch.bfloat16, (V, H), dev)
+    _need(weight, "weight", _weight_dtype(problem), (V, H), dev)
     _need(hidden, "hidden", torch.bfloat16, (T, H), dev)
     _need(labels, "labels", torch.int64, (T,), dev)
     _need(lse, "lse", torch.float32, (T,), dev)

@@ -32,22 +32,25 @@ def dev():
     return torch.device("cuda:0")
 
 
-def problem_of(inp):
+def problem_of(inp, weight_dtype=torch.bfloat16):
     X, W = inp["hidden"], inp["weight"]
     return L.make_problem(X.shape[0], X.shape[1], W.shape[0], inp["unpadded_vocab"], inp["softcap"],
-                          inp["ignore_index"], inp["reduction"], inp["num_label_tokens"])
+                          inp["ignore_index"], inp["reduction"], inp["num_label_tokens"], weight_dtype)
 
 
-def run_hip(inp, grad_out=1.0, dx_rows=None, dw_rows=None, keep_device=False):
+def run_hip(inp, grad_out=1.0, dx_rows=None, dw_rows=None, keep_device=False, fp32_head_direct=False):
     """Forward + backward through the C ABI.  Returns CPU results; dX / dW
-    are restricted to the given rows (all when None)."""
+    are restricted to the given rows (all when None).  An fp32 head is rounded
+    by flce_round_to_bf16 first, or with ``fp32_head_direct`` handed to the
+    calls as fp32 (the library stages the rounded rows itself)."""
     d = dev()
     X = inp["hidden"].to(d)
     W = inp["weight"].to(d)
     y = inp["labels"].to(d)
-    if W.dtype == torch.float32:
+    direct = fp32_head_direct and W.dtype == torch.float32
+    if W.dtype == torch.float32 and not direct:
         W = L.flce_round_to_bf16(W)
-    p = problem_of(inp)
+    p = problem_of(inp, torch.float32 if direct else torch.bfloat16)
     T, H, V = p.num_tokens, p.hidden, p.vocab
     ws = L.alloc_workspace(p, d)
     loss = torch.empty((), dtype=torch.float32, device=d)

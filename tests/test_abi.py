@@ -73,6 +73,14 @@ def test_workspace_size_bounds():
         assert code == _lib.FLCE_OK and w < T * V * 2
 
 
+def test_fp32_head_workspace_holds_the_staged_rows():
+    import torch
+    a = _ws(make_problem(8192, 3072, 262144, 256000, softcap=30.0))
+    b = _ws(make_problem(8192, 3072, 262144, 256000, softcap=30.0, weight_dtype=torch.float32))
+    assert a[0] == b[0] == _lib.FLCE_OK
+    assert b[1] - a[1] == 256000 * 3072 * 2  # bf16 copy of the usable rows only
+
+
 def test_library_source_allocates_no_device_memory():
     """The caller owns every buffer: no allocation or free call in the HIP
     sources (the workspace comes in as an argument)."""
@@ -97,7 +105,7 @@ def test_library_source_allocates_no_device_memory():
     (dict(num_label_tokens=0), _lib.FLCE_ERR_INVALID_ARG),
     (dict(hidden=100), _lib.FLCE_ERR_UNSUPPORTED),
     (dict(hidden=192), _lib.FLCE_ERR_UNSUPPORTED),
-    (dict(weight_dtype=1), _lib.FLCE_ERR_UNSUPPORTED),
+    (dict(weight_dtype=7), _lib.FLCE_ERR_UNSUPPORTED),
 ])
 def test_invalid_problem_rejected(kw, expect):
     p = make_problem(64, 128, 1000)

@@ -52,6 +52,27 @@ def test_small_full_parity(name):
     check_full(inp, res, label=name)
 
 
+def test_fp32_head_handed_over_directly():
+    """An fp32 head passed to the calls as fp32 (the library rounds and stages
+    its usable rows) gives the oracle's result and exactly the bf16-head
+    path's, bit for bit; padding rows are never read."""
+    w = SMALL["fp32_head"]
+    inp = make_inputs(w, argmax_device="cuda:0")
+    a = run_hip(inp, fp32_head_direct=True)
+    check_full(inp, a, label="fp32 head direct")
+    b = run_hip(inp)
+    assert a["loss"] == b["loss"]
+    for k in ("lse", "token_loss", "dX", "dW"):
+        assert torch.equal(a[k], b[k]), k
+    poisoned = dict(inp)
+    W = inp["weight"].clone()
+    W[w.Vu:] = float("nan")
+    poisoned["weight"] = W
+    c = run_hip(poisoned, fp32_head_direct=True)
+    for k in ("lse", "token_loss", "dX", "dW"):
+        assert torch.equal(a[k], c[k]), k
+
+
 def test_grad_out_scaling():
     w = SMALL["ragged_softcap_mean_pad"]
     inp = make_inputs(w)
@@ -181,6 +202,21 @@ def test_round_to_bf16_matches_oracle_rounding():
 # ---------------------------------------------------------------------------
 # Full-size workloads, sampled checks
 # ---------------------------------------------------------------------------
+
+
+def test_workload3_fp32_head_direct_matches_staged_cast():
+    """Softcapped padded head (fp32 head, V=262144, Vu=256000) at full size:
+    handing the fp32 head over directly is bit-identical to rounding it first
+    (the rounded path is checked against the oracle below)."""
+    w = WORKLOADS[3]
+    inp = make_inputs(w)
+    rows = np.arange(0, w.T, 97)
+    vrows = np.arange(0, w.V, 1021)
+    a = run_hip(inp, dx_rows=rows, dw_rows=vrows, fp32_head_direct=True)
+    b = run_hip(inp, dx_rows=rows, dw_rows=vrows)
+    assert a["status"] == 0 and a["loss"] == b["loss"]
+    for k in ("lse", "token_loss", "dX", "dW"):
+        assert torch.equal(a[k], b[k]), k
 
 
 @pytest.mark.parametrize("key", [2, 3, 4, 5])
