@@ -89,6 +89,35 @@ __global__ __launch_bounds__(256) void k_gather(const uint4* __restrict__ X, int
   }
 }
 
+// XcT[h][t] = Xc[t][h] through a 64 x 64 LDS tile: 16-byte reads along h,
+// 16-byte writes along t.  dW reads the gathered hidden states K-major
+// (along the tokens it sums over) from this copy.
+__global__ __launch_bounds__(256) void k_transpose_xc(const bf16* __restrict__ Xc, int64_t H, int64_t Tvp,
+                                                       bf16* __restrict__ XcT) {
+  __shared__ bf16 tile[64][64 + 2];
+  const int64_t t0 = (int64_t)blockIdx.x * 64;
+  const int64_t h0 = (int64_t)blockIdx.y * 64;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int r = pass * 32 + (tid >> 3);
+    const int c = (tid & 7) * 8;
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(Xc + (t0 + r) * H + h0 + c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[r][c + e] = v[e];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int h = pass * 32 + (tid >> 3);
+    const int c = (tid & 7) * 8;
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = tile[c + e][h];
+    *reinterpret_cast<bf16x8*>(XcT + (h0 + h) * Tvp + t0 + c) = v;
+  }
+}
+
 // Per compacted token: merge the vocab-tile partials into the log-sum-exp,
 // form the token loss, and reduce the block's losses in fp64.  A block takes
 // kCombineTokens consecutive tokens; its kCombineSlices thread rows each merge
@@ -221,7 +250,7 @@ struct Plan {
   size_t off_meta, off_valid, off_yc, off_label, off_scale, off_bsum, off_xc;
   size_t off_wst;       // bf16 staging of an fp32 head's rows < Vu (0 bytes for a bf16 head)
   size_t off_part;      // forward region
-  size_t off_g, off_hacc;  // backward region
+  size_t off_g, off_hacc, off_xct;  // backward region
   size_t total;
 };
 
@@ -320,6 +349,7 @@ Plan make_plan(const flce_problem_t* p, int n_cu = 256) {
   pl.off_g = take(pl.Tvp * ct_max * 256 * 2);
   // Every chunk width below tiles_v gives more than one chunk.
   pl.off_hacc = take(pl.tiles_v > 1 ? pl.Tvp * pl.H * 4 : 0);
+  pl.off_xct = take(pl.Tvp * pl.H * 2);
   const size_t bwd_end = o;
   pl.total = std::max(fwd_end, bwd_end);
   return pl;
@@ -514,6 +544,12 @@ int flce_backward(const flce_problem_t* problem, const void* hidden, const void*
   const bf16* W = staged_head(pl, p, weight, workspace, stream);
 
   launch_compact_gather(pl, p, labels, hidden, meta, valid_idx, yc, device_status, nullptr, nullptr, xc, stream);
+  bf16* xct = ws_at<bf16>(workspace, pl.off_xct);
+  {
+    TraceScope tr(FLCE_KERNEL_GATHER, 0.0, stream);
+    hipLaunchKernelGGL(k_transpose_xc, dim3((unsigned)(pl.Tvp / 64), (unsigned)(pl.H / 64)), dim3(256), 0, stream,
+                       (const bf16*)xc, pl.H, pl.Tvp, xct);
+  }
   {
     TraceScope tr(FLCE_KERNEL_AUX, 0.0, stream);
     hipLaunchKernelGGL(k_scale, dim3(1), dim3(1), 0, stream, grad_out, (const Meta*)meta, (int)p.reduction,
@@ -547,14 +583,15 @@ int flce_backward(const flce_problem_t* problem, const void* hidden, const void*
                            stream, A, B, sch, ep);
       }
     }
-    // 2. dW[v0 : v0 + vw] = G^T Xc   (M = chunk rows, N = H, K = tokens)
+    // 2. dW[v0 : v0 + vw] = G^T Xc   (M = chunk rows, N = H, K = tokens).
+    //    G is read MN-major (transposing LDS reads), Xc K-major from XcT.
     {
       gemm::Operand A{G, pl.vc, (int)pl.vc - 1, (int)pl.Tvp - 1};
-      gemm::Operand B{xc, pl.H, (int)pl.H - 1, (int)pl.Tvp - 1};
+      gemm::Operand B{xct, pl.Tvp, (int)pl.H - 1, 0};
       gemm::Schedule sch{(int)tiles_c, (int)pl.tiles_h, 0, tv, 3};
       epi::StoreF32::Params ep{d_weight + v0 * pl.H, pl.H, (int)vw, (int)pl.H};
       TraceScope tr(FLCE_KERNEL_DWEIGHT, chunk_flops, stream);
-      hipLaunchKernelGGL((gemm::gemm_kernel<false, false, epi::StoreF32>), dim3(tiles_c * pl.tiles_h),
+      hipLaunchKernelGGL((gemm::gemm_kernel<false, true, epi::StoreF32>), dim3(tiles_c * pl.tiles_h),
                          dim3(gemm::NTHREADS), 0, stream, A, B, sch, ep);
     }
     // 3. dH_acc (+)= G W[v0 : v0 + vw]   (M = tokens, N = H, K = chunk rows)
