@@ -94,6 +94,16 @@ struct Elt<float> {
   }
 };
 
+// Streaming 16-byte load for the forward: every logit is read once, so it
+// bypasses cache retention.  Measured on the llama3-8b logits: forward 212 ->
+// 154 us; the backward (read + write) was no faster with streaming loads or
+// stores and keeps plain ones.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 stream_load(const uint4* p) {
+  const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // Elements of a row before its first 16-byte boundary (the row may start
 // anywhere on an element boundary).
 template <class T>
@@ -162,7 +172,8 @@ __global__ __launch_bounds__(kThreads) void k_row_forward(const T* __restrict__ 
   }
   int64_t i = tid;
   for (; i + 3 * kThreads < nvec; i += 4 * kThreads) {
-    const uint4 v0 = vrow[i], v1 = vrow[i + kThreads], v2 = vrow[i + 2 * kThreads], v3 = vrow[i + 3 * kThreads];
+    const uint4 v0 = stream_load(vrow + i), v1 = stream_load(vrow + i + kThreads);
+    const uint4 v2 = stream_load(vrow + i + 2 * kThreads), v3 = stream_load(vrow + i + 3 * kThreads);
     float x[4 * E];
     Elt<T>::unpack(v0, x);
     Elt<T>::unpack(v1, x + E);
@@ -172,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void k_row_forward(const T* __restrict__ 
   }
   for (; i < nvec; i += kThreads) {
     float x[E];
-    Elt<T>::unpack(vrow[i], x);
+    Elt<T>::unpack(stream_load(vrow + i), x);
     o.add(x);
   }
   for (int64_t j = tail0 + tid; j < V; j += kThreads) {
