@@ -194,11 +194,14 @@ typedef enum flce_kernel_kind {
   FLCE_KERNEL_COMBINE = 3,      /* per-token lse / loss                       */
   FLCE_KERNEL_FINALIZE = 4,     /* loss reduction                             */
   FLCE_KERNEL_RECOMPUTE_G = 5,  /* backward logit recompute -> G chunk         */
-  FLCE_KERNEL_DWEIGHT = 6,      /* dW rows of a chunk = G^T X                  */
-  FLCE_KERNEL_DHIDDEN = 7,      /* dH += G W[chunk]                            */
+  FLCE_KERNEL_DWEIGHT = 6,      /* dW rows of a chunk = G^T X (not launched on
+                                   its own: part of FLCE_KERNEL_DGRAD)        */
+  FLCE_KERNEL_DHIDDEN = 7,      /* dH += G W[chunk] (likewise)                 */
   FLCE_KERNEL_AUX = 8,          /* zero fills, scale, rounding                 */
   FLCE_KERNEL_CE_FORWARD = 9,   /* chunked CE: per-row lse and loss            */
-  FLCE_KERNEL_CE_BACKWARD = 10  /* chunked CE: per-row logits gradient         */
+  FLCE_KERNEL_CE_BACKWARD = 10, /* chunked CE: per-row logits gradient         */
+  FLCE_KERNEL_DGRAD = 11        /* dH += G W[chunk] and dW rows = G^T X of one
+                                   chunk, in one launch; its flops are both   */
 } flce_kernel_kind_t;
 
 /*

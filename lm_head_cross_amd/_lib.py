@@ -27,7 +27,7 @@ EXPORTED = ("flce_status_string", "flce_version", "flce_workspace_size", "flce_f
             "chunked_ce_workspace_size", "chunked_ce_forward", "chunked_ce_backward", "chunked_ce_mask_labels")
 
 KERNEL_KINDS = ("compact", "gather", "proj_lse", "combine", "finalize", "recompute_g", "dweight", "dhidden",
-                "aux", "ce_forward", "ce_backward")
+                "aux", "ce_forward", "ce_backward", "dgrad")
 
 
 class Problem(ctypes.Structure):

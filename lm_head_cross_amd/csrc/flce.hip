@@ -583,29 +583,27 @@ int flce_backward(const flce_problem_t* problem, const void* hidden, const void*
                            stream, A, B, sch, ep);
       }
     }
-    // 2. dW[v0 : v0 + vw] = G^T Xc   (M = chunk rows, N = H, K = tokens).
-    //    G is read MN-major (transposing LDS reads), Xc K-major from XcT.
+    // 2. dH_acc (+)= G W[v0 : v0 + vw]   (M = tokens, N = H, K = chunk rows) and
+    //    dW[v0 : v0 + vw] = G^T Xc          (M = chunk rows, N = H, K = tokens)
+    //    in one launch, dH's tiles first.  dH's K-major G and MN-major W;
+    //    dW reads G MN-major (transposing LDS reads) and Xc K-major from XcT.
     {
-      gemm::Operand A{G, pl.vc, (int)pl.vc - 1, (int)pl.Tvp - 1};
-      gemm::Operand B{xct, pl.Tvp, (int)pl.H - 1, 0};
-      gemm::Schedule sch{(int)tiles_c, (int)pl.tiles_h, 0, tv, 3};
-      epi::StoreF32::Params ep{d_weight + v0 * pl.H, pl.H, (int)vw, (int)pl.H};
-      TraceScope tr(FLCE_KERNEL_DWEIGHT, chunk_flops, stream);
-      hipLaunchKernelGGL((gemm::gemm_kernel<false, true, epi::StoreF32>), dim3(tiles_c * pl.tiles_h),
-                         dim3(gemm::NTHREADS), 0, stream, A, B, sch, ep);
-    }
-    // 3. dH_acc (+)= G W[v0 : v0 + vw]   (M = tokens, N = H, K = chunk rows)
-    {
-      gemm::Operand A{G, pl.vc, (int)pl.Tvp - 1, 0};
-      gemm::Operand B{Wc, pl.H, (int)pl.H - 1, (int)vw - 1};
-      gemm::Schedule sch{(int)pl.tiles_t, (int)pl.tiles_h, k_steps_for(vw), tv, 1};
+      gemm::Operand Ah{G, pl.vc, (int)pl.Tvp - 1, 0};
+      gemm::Operand Bh{Wc, pl.H, (int)pl.H - 1, (int)vw - 1};
+      gemm::Schedule sh{(int)pl.tiles_t, (int)pl.tiles_h, k_steps_for(vw), tv, 1};
       int mode = 0;
       if (c == 0) mode |= epi::kAccFirst;
       if (c == pl.nchunks - 1) mode |= epi::kAccLast;
-      epi::AccumH::Params ep{hacc, pl.H, (bf16*)d_hidden, valid_idx, tv, (int)pl.H, mode};
-      TraceScope tr(FLCE_KERNEL_DHIDDEN, chunk_flops, stream);
-      hipLaunchKernelGGL((gemm::gemm_kernel<true, false, epi::AccumH>), dim3(pl.tiles_t * pl.tiles_h),
-                         dim3(gemm::NTHREADS), 0, stream, A, B, sch, ep);
+      epi::AccumH::Params eh{hacc, pl.H, (bf16*)d_hidden, valid_idx, tv, (int)pl.H, mode};
+      gemm::Operand Aw{G, pl.vc, (int)pl.vc - 1, (int)pl.Tvp - 1};
+      gemm::Operand Bw{xct, pl.Tvp, (int)pl.H - 1, 0};
+      gemm::Schedule sw{(int)tiles_c, (int)pl.tiles_h, 0, tv, 3};
+      epi::StoreF32::Params ew{d_weight + v0 * pl.H, pl.H, (int)vw, (int)pl.H};
+      const int64_t n_h = align_up((size_t)(pl.tiles_t * pl.tiles_h), 8);
+      TraceScope tr(FLCE_KERNEL_DGRAD, 2.0 * chunk_flops, stream);
+      hipLaunchKernelGGL((gemm::gemm_pair<true, false, epi::AccumH, false, true, epi::StoreF32>),
+                         dim3(n_h + tiles_c * pl.tiles_h), dim3(gemm::NTHREADS), 0, stream, Ah, Bh, sh, eh, (int)n_h,
+                         Aw, Bw, sw, ew);
     }
   }
   return launch_status();

@@ -399,17 +399,14 @@ __device__ __forceinline__ int acc_row(int wm, int mb, int r, int lane) {
 }
 __device__ __forceinline__ int acc_col(int wn, int nb, int lane) { return wn * 128 + 32 * nb + (lane & 31); }
 
-// The kernel: schedule, early exit for tiles past the valid tokens, main loop,
+// One tile: schedule, early exit for tiles past the valid tokens, main loop,
 // then the epilogue (which may reuse the first stage's LDS).
 template <bool A_KMAJOR, bool B_KMAJOR, class Epi>
-__global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(Operand A, Operand B, Schedule sch,
-                                                            typename Epi::Params ep) {
-  __shared__ __attribute__((aligned(1024))) bf16 s0[STAGE_ELEMS];
-  __shared__ __attribute__((aligned(1024))) bf16 s1[STAGE_ELEMS];
-  __shared__ __attribute__((aligned(1024))) bf16 s2[STAGE_ELEMS];
-  __shared__ __attribute__((aligned(1024))) bf16 s3[STAGE_ELEMS];
+__device__ __forceinline__ void run_tile(const Operand& A, const Operand& B, const Schedule& sch,
+                                         const typename Epi::Params& ep, int pid, bf16* s0, bf16* s1, bf16* s2,
+                                         bf16* s3) {
   int tm, tn;
-  tile_of(blockIdx.x, sch.tiles_m, sch.tiles_n, tm, tn);
+  tile_of(pid, sch.tiles_m, sch.tiles_n, tm, tn);
   const int m0 = tm * BM;
   const int n0 = tn * BN;
   int k_steps = sch.k_steps;
@@ -422,6 +419,39 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(Operand A, Operand B,
   f32x16 acc[4][4];
   mainloop<A_KMAJOR, B_KMAJOR>(A, B, m0, n0, k_steps, s0, s1, s2, s3, acc);
   Epi::apply(ep, acc, m0, n0, s0);
+}
+
+template <bool A_KMAJOR, bool B_KMAJOR, class Epi>
+__global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(Operand A, Operand B, Schedule sch,
+                                                            typename Epi::Params ep) {
+  __shared__ __attribute__((aligned(1024))) bf16 s0[STAGE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 s1[STAGE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 s2[STAGE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 s3[STAGE_ELEMS];
+  run_tile<A_KMAJOR, B_KMAJOR, Epi>(A, B, sch, ep, blockIdx.x, s0, s1, s2, s3);
+}
+
+// Two independent GEMMs in one launch: workgroups [0, n1) take the first
+// problem's tiles (n1 is its tile count rounded up to a multiple of 8, so
+// that the second problem's tiles keep the id-to-XCD mapping tile_of
+// assumes), the rest the second's.  The hardware hands out workgroups in id
+// order, so compute units that finish the first problem's last, partly
+// filled round of tiles go on to the second problem at once.
+template <bool A1_KMAJOR, bool B1_KMAJOR, class Epi1, bool A2_KMAJOR, bool B2_KMAJOR, class Epi2>
+__global__ __launch_bounds__(NTHREADS, 1) void gemm_pair(Operand A1, Operand B1, Schedule sch1,
+                                                          typename Epi1::Params ep1, int n1, Operand A2, Operand B2,
+                                                          Schedule sch2, typename Epi2::Params ep2) {
+  __shared__ __attribute__((aligned(1024))) bf16 s0[STAGE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 s1[STAGE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 s2[STAGE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 s3[STAGE_ELEMS];
+  const int pid = blockIdx.x;
+  if (pid < n1) {
+    if (pid < sch1.tiles_m * sch1.tiles_n)
+      run_tile<A1_KMAJOR, B1_KMAJOR, Epi1>(A1, B1, sch1, ep1, pid, s0, s1, s2, s3);
+  } else {
+    run_tile<A2_KMAJOR, B2_KMAJOR, Epi2>(A2, B2, sch2, ep2, pid - n1, s0, s1, s2, s3);
+  }
 }
 
 }  // namespace gemm
