@@ -6,34 +6,30 @@
 // v_mfma_f32_32x32x16_bf16 instruction, whose fp32 accumulators live in the
 // AGPR half of the register file (one wave per SIMD).
 //
-// With both operands K-major (the projection and the recompute), K advances
-// 64 at a time through two 64 KB LDS stages (mainloop64, described there).
-// Otherwise K advances 32 at a time through four LDS stages of 32 KB (A and B
-// tiles of 16 KB each), each its own __shared__ array.  Stages are filled by
-// buffer_load_dwordx4 ... lds, which writes each lane's 16 bytes straight
-// into LDS (no VGPR staging, no LDS write instructions), three stages ahead
-// of the stage being multiplied and spread across a stage's MFMAs.  Separate
-// arrays let the compiler see that a DMA in flight never aliases the stage
-// being read, so it does not stall LDS reads on it; the wait before each
-// workgroup barrier names how many DMA instructions may still be
-// outstanding.
-//
-// The MFMA fragments of the next stage (both 16-wide k steps) are read while
-// the current stage's 32 MFMAs issue, into four register sets that rotate
-// every two stages.  One barrier per stage, at its start, hands the next
-// stage over.
+// K advances 64 at a time through two LDS stages of 64 KB: A in the arrays
+// s0 / s2, B in s1 / s3, each array its own __shared__ object so that the
+// compiler can see that a DMA in flight into one stage never aliases the
+// stage being read (it then does not make the LDS reads wait for it).
+// Stages are filled by buffer_load_dwordx4 ... lds, which writes each lane's
+// 16 bytes straight into LDS (no VGPR staging, no LDS write instructions),
+// spread between the MFMAs.  A stage runs as four k steps of 16, 16 MFMAs
+// per wave each; one workgroup barrier per stage hands the next stage over.
 //
 // Either operand may be K-major (element (mn, k) at ptr[mn*ld + k]) or
 // MN-major (element (mn, k) at ptr[k*ld + mn]); the LDS tile keeps the
 // global layout, so global loads stay fully coalesced either way:
-//  - K-major tile: 256 rows x 32 k (64-byte rows).  A fragment (one row,
-//    8 consecutive k) is one ds_read_b128.  The 16-byte chunk c of row r sits
-//    at chunk c ^ swz_k(r), which leaves these reads free of bank conflicts.
-//  - MN-major tile: 32 k-rows x 256 mn (512-byte rows).  A fragment is two
+//  - K-major tile: 256 rows x 64 k, rows of 128 bytes, so every DMA moves
+//    whole cache lines.  A fragment (one row, 8 consecutive k) is one
+//    ds_read_b128.  The 16-byte chunk c of row r sits at slot c ^ swz64(r).
+//  - MN-major tile: 64 k-rows x 256 mn (512-byte rows).  A fragment is two
 //    ds_read_b64_tr_b16: within each 16-lane group the hardware transposes a
 //    4 (k) x 16 (mn) block so that lane i receives column i, four
 //    consecutive k.  Pairs of 16-byte chunks are XOR-swizzled per k-row,
 //    which leaves these reads free of bank conflicts.
+// With both operands K-major (the projection and the recompute) fragments
+// are read one k step ahead (mainloop_kk); with an MN-major operand (dH, dW)
+// two k steps ahead, since the transposing reads take a few hundred cycles
+// under load (mainloop_mn).
 //
 // The accumulator layout of the 32x32 MFMA: lane l, register r holds element
 // (row 8*(r/4) + 4*(l/32) + r%4, column l%32) of its block.
@@ -46,14 +42,11 @@ namespace gemm {
 
 constexpr int BM = 256;
 constexpr int BN = 256;
-constexpr int BK = 32;
-constexpr int NST = 4;                        // LDS stages
-constexpr int SUB = BK / 16;                  // MFMA k steps per stage
+constexpr int BK = 32;                        // K is counted in steps of 32 (Schedule::k_steps) ...
+constexpr int NST = 4;                        // ... and padded to a multiple of NST steps (128)
+constexpr int BK2 = 64;                       // k per LDS stage
 constexpr int NTHREADS = 256;
-constexpr int TILE_ELEMS = 256 * BK;          // one operand, one stage (16 KB)
-constexpr int STAGE_ELEMS = 2 * TILE_ELEMS;   // A + B (32 KB)
-constexpr int LOADS_PER_STAGE = STAGE_ELEMS * 2 / 16 / NTHREADS;  // DMA instructions per thread (8)
-constexpr int LOADS_PER_TILE = LOADS_PER_STAGE / 2;               // per operand (4)
+constexpr int STAGE_ELEMS = 256 * BK2;        // one operand's tile of one stage (32 KB)
 
 // One GEMM operand.
 struct Operand {
@@ -71,13 +64,14 @@ struct Schedule {
   int tok_dim;              // 0: none, 1: M is tokens, 2: N is tokens, 3: K is tokens
 };
 
-// Chosen by measurement (SQ_LDS_BANK_CONFLICT on gfx950 for this exact
-// read pattern): XOR-ing chunks with bits 2..3 of the row leaves the
-// ds_read_b128 of both k steps conflict-free.
-__device__ __forceinline__ int swz_k(int r) { return (r >> 2) & 3; }
+// Chunk slot of a K-major row: chunk c of row r sits at c ^ swz64(r), which
+// keeps the 8- and 16-lane phases of a fragment read (consecutive rows, one
+// chunk) on distinct banks.
+__device__ __forceinline__ int swz64(int r) { return (r >> 1) & 7; }
 
 // Chunk XOR for MN-major rows: pairs of 16-byte chunks are XOR-ed with
 // t(k % 4) in {0, 3, 5, 6}; t and t ^ 1 cover all eight pair slots of 256 B.
+// Chosen by measuring SQ_LDS_BANK_CONFLICT for this read pattern: 0.
 __device__ __forceinline__ int swz_mn(int k) { return ((0x6530 >> ((k & 3) * 4)) & 0xF) << 1; }
 
 // Global -> LDS copy of 16 bytes per lane through a buffer resource: the
@@ -101,7 +95,7 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 
 // Workgroup barrier after this wave's DMA instructions older than the newest
 // `n_out` have landed and its LDS reads are done.  A fence-based barrier
-// would also wait for the DMAs still in flight into the other stages.
+// would also wait for the DMAs still in flight into the other stage.
 template <int N_OUT>
 __device__ __forceinline__ void stage_barrier() {
   wait_vm_lgkm0<N_OUT>();
@@ -110,22 +104,22 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Per-thread DMA sources for one operand, fixed along K: the byte offset of
-// each of this thread's 16-byte pieces relative to the tile's origin.
-//  - K-major: resource based at the tile's first row; stage k0 adds 2*k0
-//    bytes through the scalar offset.
-//  - MN-major: resource rebased at k-row k0 for every stage (scalar work);
-//    rows past k_max read as zero (the partner operand is zero there too).
+// Per-thread DMA sources of one operand for 64-wide stages, fixed along K:
+// the byte offset of each of this thread's 16-byte pieces (8 blocks of 1 KB
+// per wave) relative to the tile's origin.
+//  - K-major: a block is 8 rows x 128 B; the resource is based at the tile's
+//    first row, and stage k0 adds 2*k0 bytes through the scalar offset.
+//  - MN-major: a block is 2 k-rows x 512 B; the resource is rebased at k-row
+//    k0 for every stage (scalar work), and rows past k_max read as zero (the
+//    partner operand is zero there too).
 template <bool KMAJOR>
 struct Loader {
   const bf16* base;
   int64_t ld;
   int k_max;
-  __amdgpu_buffer_rsrc_t rsrc;      // K-major only
-  unsigned off[LOADS_PER_TILE];     // bytes
-  int kk[LOADS_PER_TILE];           // MN-major: k row within the stage
-  int col[LOADS_PER_TILE];          // MN-major: column (elements)
-
+  __amdgpu_buffer_rsrc_t rsrc;
+  unsigned off[8];
+  int kk[8];
   __device__ __forceinline__ Loader(const Operand& op, int mn0, int wave, int lane) {
     ld = op.ld;
     k_max = op.k_max;
@@ -133,60 +127,55 @@ struct Loader {
       base = op.ptr + (int64_t)mn0 * op.ld;
       rsrc = make_rsrc(base);
 #pragma unroll
-      for (int q = 0; q < LOADS_PER_TILE; ++q) {
-        const int b = wave * LOADS_PER_TILE + q;   // 1 KB block: 16 rows of 64 B
-        const int r = b * 16 + (lane >> 2);
-        const int c = (lane & 3) ^ swz_k(r);
+      for (int q = 0; q < 8; ++q) {
+        const int b = wave * 8 + q;
+        const int r = b * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swz64(r);
         const int gr = min(mn0 + r, op.mn_max) - mn0;
         off[q] = (unsigned)(gr * (int)op.ld + c * 8) * 2u;
         kk[q] = 0;
-        col[q] = 0;
       }
     } else {
       base = op.ptr;
       rsrc = make_rsrc(base);
 #pragma unroll
-      for (int q = 0; q < LOADS_PER_TILE; ++q) {
-        const int b = wave * LOADS_PER_TILE + q;   // 1 KB block: 2 k-rows of 512 B
+      for (int q = 0; q < 8; ++q) {
+        const int b = wave * 8 + q;            // 1 KB block: 2 k-rows of 512 B
         kk[q] = b * 2 + (lane >> 5);
         const int c = (lane & 31) ^ swz_mn(kk[q]);
-        col[q] = min(mn0 + c * 8, op.mn_max - 7);
-        off[q] = (unsigned)(kk[q] * (int)op.ld + col[q]) * 2u;
+        const int col = min(mn0 + c * 8, op.mn_max - 7);
+        off[q] = (unsigned)(kk[q] * (int)op.ld + col) * 2u;
       }
     }
   }
-
-  // Issue this thread's share of the stage starting at k0 into `tile`.
+  template <int Q0, int Q1>
   __device__ __forceinline__ void issue(bf16* tile, int k0, int wave) const {
     if constexpr (KMAJOR) {
       const unsigned soff = (unsigned)k0 * 2u;
 #pragma unroll
-      for (int q = 0; q < LOADS_PER_TILE; ++q)
-        lds_dma16(rsrc, off[q], soff, tile + (wave * LOADS_PER_TILE + q) * 512);
+      for (int q = Q0; q < Q1; ++q) lds_dma16(rsrc, off[q], soff, tile + (wave * 8 + q) * 512);
     } else {
       const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (int64_t)k0 * ld);
-      if (k0 + BK - 1 <= k_max) {
+      if (k0 + BK2 - 1 <= k_max) {
 #pragma unroll
-        for (int q = 0; q < LOADS_PER_TILE; ++q)
-          lds_dma16(r, off[q], 0, tile + (wave * LOADS_PER_TILE + q) * 512);
+        for (int q = Q0; q < Q1; ++q) lds_dma16(r, off[q], 0, tile + (wave * 8 + q) * 512);
       } else {
-        // Rows past k_max read as zero: their offsets are made out of range,
-        // which the buffer unit answers with zeros and no memory access.
         const int krem = k_max - k0;
 #pragma unroll
-        for (int q = 0; q < LOADS_PER_TILE; ++q) {
+        for (int q = Q0; q < Q1; ++q) {
           const unsigned o = kk[q] <= krem ? off[q] : 0x80000000u;
-          lds_dma16(r, o, 0, tile + (wave * LOADS_PER_TILE + q) * 512);
+          lds_dma16(r, o, 0, tile + (wave * 8 + q) * 512);
         }
       }
     }
   }
 };
 
-// Fragment of a K-major tile: row `row` (0..255), k = 16*s + 8*(lane/32) + 0..7.
-__device__ __forceinline__ bf16x8 frag_kmajor(const bf16* tile, int row, int s, int lane) {
-  const int c = (2 * s + (lane >> 5)) ^ swz_k(row);
-  return *(const FLCE_LDS bf16x8*)(tile + row * BK + c * 8);
+
+// Fragment of a 64-wide K-major tile: row `row`, k = 16*s + 8*(lane/32) + 0..7.
+__device__ __forceinline__ bf16x8 frag64(const bf16* tile, int row, int s, int lane) {
+  const int c = (2 * s + (lane >> 5)) ^ swz64(row);
+  return *(const FLCE_LDS bf16x8*)(tile + row * BK2 + c * 8);
 }
 
 // Fragment of an MN-major tile for the 32 columns starting at col0:
@@ -212,19 +201,18 @@ __device__ __forceinline__ bf16x8 frag_mnmajor(const bf16* tile, int col0, int s
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// This wave's fragments of k step s: rows wm*128 + 32*i (A), wn*128 + 32*i (B).
 template <bool A_KMAJOR, bool B_KMAJOR>
-__device__ __forceinline__ void read_frags(const bf16* stage, int s, int wm, int wn, int lane, bf16x8 (&fa)[4],
-                                           bf16x8 (&fb)[4]) {
-  const bf16* sa = stage;
-  const bf16* sb = stage + TILE_ELEMS;
+__device__ __forceinline__ void read_frags(const bf16* sa, const bf16* sb, int s, int wm, int wn, int lane,
+                                            bf16x8 (&fa)[4], bf16x8 (&fb)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if constexpr (A_KMAJOR) fa[i] = frag_kmajor(sa, wm * 128 + 32 * i + (lane & 31), s, lane);
+    if constexpr (A_KMAJOR) fa[i] = frag64(sa, wm * 128 + 32 * i + (lane & 31), s, lane);
     else fa[i] = frag_mnmajor(sa, wm * 128 + 32 * i, s, lane);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if constexpr (B_KMAJOR) fb[i] = frag_kmajor(sb, wn * 128 + 32 * i + (lane & 31), s, lane);
+    if constexpr (B_KMAJOR) fb[i] = frag64(sb, wn * 128 + 32 * i + (lane & 31), s, lane);
     else fb[i] = frag_mnmajor(sb, wn * 128 + 32 * i, s, lane);
   }
 }
@@ -266,32 +254,10 @@ constexpr int kSchedMfma = 0x008;
 constexpr int kSchedVmemRead = 0x020;
 constexpr int kSchedDsRead = 0x100;
 
-// s_waitcnt vmcnt <= VM, lgkmcnt <= LG, then the workgroup barrier.
-template <int VM, int LG>
-__device__ __forceinline__ void stage_barrier_lg() {
-  static_assert(VM >= 0 && VM < 64 && LG >= 0 && LG < 16, "waitcnt range");
-  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (LG << 8));
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// One stage of the main loop.  Stage j's fragments (both k steps) were read
-// during stage j-1 into register sets U0, U1; this stage reads stage j+1's
-// into R0, R1 while its 32 MFMAs issue, and refills the buffer of stage j-1
-// with stage `refill_step` (A half during the first k step, B half during
-// the second).
-//  - The barrier at the start makes stage j+1 visible (WAIT_OUT: this
-//    thread's DMA instructions that may still be in flight, those issued
-//    after stage j+1's) and frees stage j-1's buffer: every wave finished
-//    its reads of stage j-1 before the LDS reads of stage j it issued last,
-//    and LDS reads complete in order, so the wait may leave this stage's own
-//    2*NR reads outstanding (capped by the 4-bit lgkmcnt field).
-//  - HAS_NEXT: there is a stage j+1.  REFILL: there is a stage to issue.
-// Instruction order is pinned per k step: LDS reads and DMAs spread evenly
-// between the 16 MFMAs.  A DMA issue can stall the wave while the address
-// unit is busy, and a stalled wave issues no MFMA, so no two DMAs sit next
-// to each other.
+// Instruction order is pinned per k step: NR LDS reads and NV DMAs spread
+// evenly between the 16 MFMAs.  A DMA issue can stall the wave while the
+// address unit is busy, and a stalled wave issues no MFMA, so no two DMAs sit
+// next to each other.
 template <int NR, int NV>
 __device__ __forceinline__ void interleave_step() {
 #pragma unroll
@@ -303,170 +269,27 @@ __device__ __forceinline__ void interleave_step() {
   }
 }
 
-template <bool A_KMAJOR, bool B_KMAJOR, int WAIT_OUT, bool HAS_NEXT, bool REFILL, int U0, int U1, int R0, int R1,
-          class LA, class LB>
-__device__ __forceinline__ void stage_compute(bf16* nxt, bf16* refill, int refill_step, const LA& la, const LB& lb,
-                                              int wave, int wm, int wn, int lane, bf16x8 (&fa)[4][4],
-                                              bf16x8 (&fb)[4][4], f32x16 (&acc)[4][4]) {
-  constexpr int NR = frag_reads<A_KMAJOR, B_KMAJOR>();
-  constexpr int LG = 2 * NR < 15 ? 2 * NR : 15;
-  constexpr int NRD = HAS_NEXT ? NR : 0;
-  constexpr int NV = REFILL ? LOADS_PER_TILE : 0;
-  if constexpr (HAS_NEXT) {
-    stage_barrier_lg<WAIT_OUT, LG>();
-    read_frags<A_KMAJOR, B_KMAJOR>(nxt, 0, wm, wn, lane, fa[R0], fb[R0]);
-  }
-  if constexpr (REFILL) la.issue(refill, refill_step * BK, wave);
-  mfma_step(fa[U0], fb[U0], acc);
-  interleave_step<NRD, NV>();
-  __builtin_amdgcn_sched_barrier(0);
-  if constexpr (HAS_NEXT) read_frags<A_KMAJOR, B_KMAJOR>(nxt, 1, wm, wn, lane, fa[R1], fb[R1]);
-  if constexpr (REFILL) lb.issue(refill + TILE_ELEMS, refill_step * BK, wave);
-  mfma_step(fa[U1], fb[U1], acc);
-  interleave_step<NRD, NV>();
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// The main loop over nk stages of BK; nk must be a multiple of NST (callers
-// pad K to NST * BK with operands that are zero there).  acc[mb][nb] is the
-// 32x32 block at rows wm*128 + 32*mb, columns wn*128 + 32*nb of the tile.
+// ---- Both operands K-major: fragments one k step ahead (two register sets).
+// Stage D+1's DMAs go out over the last k step of stage D-1 and the first two
+// of stage D.  At the start of stage D's last k step one barrier (after
+// vmcnt(0), lgkmcnt(0)) makes D+1 visible everywhere and frees D's buffer,
+// whose refill with stage D+2 starts right there.
 //
-// Stage j lives in buffer j % 4.  Stages 0..2 are issued up front; stage
-// j+3 is issued during stage j into the buffer of stage j-1, so a DMA has
-// about two stages of MFMA time to land.  Fragments are read a whole stage
-// (two k steps) ahead: the transposing LDS reads of MN-major operands take
-// a few hundred cycles under load, more than one k step of MFMAs covers.
-// Stage j's k steps use register sets (2j) % 4 and (2j+1) % 4, so the
-// pattern repeats every two stages and the loop unrolls over the four
-// buffers.
-template <bool A_KMAJOR, bool B_KMAJOR>
-__device__ __forceinline__ void mainloop(const Operand& A, const Operand& B, int m0, int n0, int nk, bf16* s0,
-                                         bf16* s1, bf16* s2, bf16* s3, f32x16 (&acc)[4][4]) {
-  const int tid = threadIdx.x;
-  // Wave-uniform in an SGPR, so LDS destinations of the DMAs are scalar.
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
-
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-  if (nk <= 0) return;
-
-  const Loader<A_KMAJOR> la(A, m0, wave, lane);
-  const Loader<B_KMAJOR> lb(B, n0, wave, lane);
-  auto dma = [&](bf16* stage, int step) {
-    la.issue(stage, step * BK, wave);
-    lb.issue(stage + TILE_ELEMS, step * BK, wave);
-  };
-  constexpr int L = LOADS_PER_STAGE;
-
-  // Prologue: stages 0..2 in flight; stage 0's fragments read.
-  dma(s0, 0);
-  dma(s1, 1);
-  dma(s2, 2);
-  stage_barrier<2 * L>();
-  bf16x8 fa[4][4], fb[4][4];
-  read_frags<A_KMAJOR, B_KMAJOR>(s0, 0, wm, wn, lane, fa[0], fb[0]);
-  read_frags<A_KMAJOR, B_KMAJOR>(s0, 1, wm, wn, lane, fa[1], fb[1]);
-
-  // At the barrier of stage it+J, stage it+J+1 must have landed; stage
-  // it+J+2 may still be in flight.
-#define FLCE_STAGE(J, REFILL, HAS_NEXT, WAIT)                                                                   \
-  stage_compute<A_KMAJOR, B_KMAJOR, WAIT, HAS_NEXT, REFILL, (2 * (J)) % 4, (2 * (J) + 1) % 4, (2 * (J) + 2) % 4, \
-                (2 * (J) + 3) % 4>((J) == 0 ? s1 : (J) == 1 ? s2 : (J) == 2 ? s3 : s0,                           \
-                                   (J) == 0 ? s3 : (J) == 1 ? s0 : (J) == 2 ? s1 : s2, it + (J) + 3, la, lb, wave, \
-                                   wm, wn, lane, fa, fb, acc)
-  int it = 0;
-  for (; it + NST < nk; it += NST) {
-    FLCE_STAGE(0, true, true, L);
-    FLCE_STAGE(1, true, true, L);
-    FLCE_STAGE(2, true, true, L);
-    FLCE_STAGE(3, true, true, L);
-  }
-  // Last four stages: one refill left, then the in-flight count drains.
-  FLCE_STAGE(0, true, true, L);
-  FLCE_STAGE(1, false, true, L);
-  FLCE_STAGE(2, false, true, 0);
-  FLCE_STAGE(3, false, false, 0);
-#undef FLCE_STAGE
-  stage_barrier<0>();
-}
-
-
-// ---- The K x K main loop: 64-wide k stages, two LDS buffers. ----
-//
-// With both operands K-major, a 32-wide k stage gives every row a 64-byte
-// piece, so each 1 KB DMA instruction covers 16 half cache lines; the address
-// path then spends about 33 cycles per instruction (TA_BUSY against the DMA
-// count), and 32 of them per 1024 MFMA cycles leave it saturated.  With
-// 64-wide stages each DMA covers 8 whole 128-byte lines.  Measured on the
+// Why 64-wide stages: with 32-wide ones every row of a K-major tile is a
+// 64-byte piece, so each 1 KB DMA covers 16 half cache lines; the address
+// unit then spent about 33 cycles per DMA (TA_BUSY over the DMA count) and 32
+// of them per 1024 MFMA cycles kept it saturated.  Measured on the
 // projection, recompute and a square shape: 7.5-10.6% faster than the
-// four-buffer 32-wide loop below.
+// earlier four-buffer 32-wide loop.
 //
-// A stage of 64 k is 64 KB (A and B, 256 rows x 128 B each), so LDS holds two:
-// A in s0 / s2, B in s1 / s3, each its own array (own alias scope).  A stage
-// runs as four k steps of 16 (16 MFMAs per wave each); fragments are read one
-// k step ahead from LDS with ds_read_b128.  Stage D+1's DMAs go out over the
-// last k step of stage D-1 and the first two of stage D; at the start of
-// stage D's last k step one barrier (after vmcnt(0), lgkmcnt(0)) makes D+1
-// visible everywhere and frees D's buffer, whose refill with stage D+2 starts
-// right there.  Rows of 128 B hold 8 chunks of 16 B; chunk c of row r sits at
-// slot c ^ ((r >> 1) & 7), which keeps the 8- and 16-lane phases of a
-// fragment read (consecutive rows, one chunk) on distinct banks.
-constexpr int BK2 = 64;
-__device__ __forceinline__ int swz64(int r) { return (r >> 1) & 7; }
-
-// Per-thread DMA sources of one K-major operand for 64-wide stages: 8 blocks
-// of 1 KB (8 rows x 128 B) per wave; stage k0 adds 2*k0 bytes through the
-// scalar offset.
-struct Loader64 {
-  __amdgpu_buffer_rsrc_t rsrc;
-  unsigned off[8];
-  __device__ __forceinline__ Loader64(const Operand& op, int mn0, int wave, int lane) {
-    rsrc = make_rsrc(op.ptr + (int64_t)mn0 * op.ld);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int b = wave * 8 + q;
-      const int r = b * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ swz64(r);
-      const int gr = min(mn0 + r, op.mn_max) - mn0;
-      off[q] = (unsigned)(gr * (int)op.ld + c * 8) * 2u;
-    }
-  }
-  // Blocks [Q0, Q1) of this wave's share of the stage starting at k0.
-  template <int Q0, int Q1>
-  __device__ __forceinline__ void issue(bf16* tile, int k0, int wave) const {
-    const unsigned soff = (unsigned)k0 * 2u;
-#pragma unroll
-    for (int q = Q0; q < Q1; ++q) lds_dma16(rsrc, off[q], soff, tile + (wave * 8 + q) * 512);
-  }
-};
-
-// Fragment of a 64-wide K-major tile: row `row`, k = 16*s + 8*(lane/32) + 0..7.
-__device__ __forceinline__ bf16x8 frag64(const bf16* tile, int row, int s, int lane) {
-  const int c = (2 * s + (lane >> 5)) ^ swz64(row);
-  return *(const FLCE_LDS bf16x8*)(tile + row * BK2 + c * 8);
-}
-
-__device__ __forceinline__ void read_frags64(const bf16* sa, const bf16* sb, int s, int wm, int wn, int lane,
-                                             bf16x8 (&fa)[4], bf16x8 (&fb)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) fa[i] = frag64(sa, wm * 128 + 32 * i + (lane & 31), s, lane);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) fb[i] = frag64(sb, wn * 128 + 32 * i + (lane & 31), s, lane);
-}
-
 // Stage D in buffers (ca, cb), stage D+1 in (na, nb).  NEXT: there is a stage
 // D+1 (whose remaining DMAs go out in k steps 0 and 1).  NEXT2: there is a
 // stage D+2 (its first DMAs go out in k step 3, into (ca, cb)).
 template <bool NEXT, bool NEXT2>
-__device__ __forceinline__ void stage64(bf16* ca, bf16* cb, bf16* na, bf16* nb, int D, const Loader64& la,
-                                        const Loader64& lb, int wave, int wm, int wn, int lane,
+__device__ __forceinline__ void stage_kk(bf16* ca, bf16* cb, bf16* na, bf16* nb, int D, const Loader<true>& la,
+                                        const Loader<true>& lb, int wave, int wm, int wn, int lane,
                                         bf16x8 (&fa)[2][4], bf16x8 (&fb)[2][4], f32x16 (&acc)[4][4]) {
-  read_frags64(ca, cb, 1, wm, wn, lane, fa[1], fb[1]);
+  read_frags<true, true>(ca, cb, 1, wm, wn, lane, fa[1], fb[1]);
   if constexpr (NEXT) {
     la.issue<6, 8>(na, (D + 1) * BK2, wave);
     lb.issue<0, 3>(nb, (D + 1) * BK2, wave);
@@ -475,20 +298,20 @@ __device__ __forceinline__ void stage64(bf16* ca, bf16* cb, bf16* na, bf16* nb, 
   interleave_step<8, NEXT ? 5 : 0>();
   __builtin_amdgcn_sched_barrier(0);
 
-  read_frags64(ca, cb, 2, wm, wn, lane, fa[0], fb[0]);
+  read_frags<true, true>(ca, cb, 2, wm, wn, lane, fa[0], fb[0]);
   if constexpr (NEXT) lb.issue<3, 8>(nb, (D + 1) * BK2, wave);
   mfma_step(fa[1], fb[1], acc);
   interleave_step<8, NEXT ? 5 : 0>();
   __builtin_amdgcn_sched_barrier(0);
 
-  read_frags64(ca, cb, 3, wm, wn, lane, fa[1], fb[1]);
+  read_frags<true, true>(ca, cb, 3, wm, wn, lane, fa[1], fb[1]);
   mfma_step(fa[0], fb[0], acc);
   interleave_step<8, 0>();
   __builtin_amdgcn_sched_barrier(0);
 
   if constexpr (NEXT) {
     stage_barrier<0>();
-    read_frags64(na, nb, 0, wm, wn, lane, fa[0], fb[0]);
+    read_frags<true, true>(na, nb, 0, wm, wn, lane, fa[0], fb[0]);
     if constexpr (NEXT2) la.issue<0, 6>(ca, (D + 2) * BK2, wave);
   }
   mfma_step(fa[1], fb[1], acc);
@@ -498,7 +321,7 @@ __device__ __forceinline__ void stage64(bf16* ca, bf16* cb, bf16* na, bf16* nb, 
 
 // nk counts 32-wide steps and is a multiple of NST, so there is an even
 // number (at least two) of 64-wide stages.
-__device__ __forceinline__ void mainloop64(const Operand& A, const Operand& B, int m0, int n0, int nk, bf16* s0,
+__device__ __forceinline__ void mainloop_kk(const Operand& A, const Operand& B, int m0, int n0, int nk, bf16* s0,
                                            bf16* s1, bf16* s2, bf16* s3, f32x16 (&acc)[4][4]) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -511,8 +334,8 @@ __device__ __forceinline__ void mainloop64(const Operand& A, const Operand& B, i
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
   if (nk <= 0) return;
   const int nd = nk / 2;
-  const Loader64 la(A, m0, wave, lane);
-  const Loader64 lb(B, n0, wave, lane);
+  const Loader<true> la(A, m0, wave, lane);
+  const Loader<true> lb(B, n0, wave, lane);
   // Prologue: stage 0 whole, the first part of stage 1 (the rest goes out in
   // stage 0's first two k steps, as in the steady state).
   la.issue<0, 8>(s0, 0, wave);
@@ -520,14 +343,89 @@ __device__ __forceinline__ void mainloop64(const Operand& A, const Operand& B, i
   la.issue<0, 6>(s2, BK2, wave);
   stage_barrier<6>();
   bf16x8 fa[2][4], fb[2][4];
-  read_frags64(s0, s1, 0, wm, wn, lane, fa[0], fb[0]);
+  read_frags<true, true>(s0, s1, 0, wm, wn, lane, fa[0], fb[0]);
   int D = 0;
   for (; D + 2 < nd; D += 2) {
-    stage64<true, true>(s0, s1, s2, s3, D, la, lb, wave, wm, wn, lane, fa, fb, acc);
-    stage64<true, true>(s2, s3, s0, s1, D + 1, la, lb, wave, wm, wn, lane, fa, fb, acc);
+    stage_kk<true, true>(s0, s1, s2, s3, D, la, lb, wave, wm, wn, lane, fa, fb, acc);
+    stage_kk<true, true>(s2, s3, s0, s1, D + 1, la, lb, wave, wm, wn, lane, fa, fb, acc);
   }
-  stage64<true, false>(s0, s1, s2, s3, D, la, lb, wave, wm, wn, lane, fa, fb, acc);
-  stage64<false, false>(s2, s3, s0, s1, D + 1, la, lb, wave, wm, wn, lane, fa, fb, acc);
+  stage_kk<true, false>(s0, s1, s2, s3, D, la, lb, wave, wm, wn, lane, fa, fb, acc);
+  stage_kk<false, false>(s2, s3, s0, s1, D + 1, la, lb, wave, wm, wn, lane, fa, fb, acc);
+  stage_barrier<0>();
+}
+
+// ---- An MN-major operand (dH, dW): fragments two k steps ahead, into four
+// register sets, one per k step of a stage.  The barrier sits at the start of
+// k step 2, where stage D+1's first fragments are read; stage D+1's DMAs go
+// out in k steps 2 and 3 of stage D-1 and k step 0 of stage D.  Against the
+// earlier 32-wide four-buffer loop: dH 1.2% and dW 1.7% faster.
+template <bool A_KMAJOR, bool B_KMAJOR, bool NEXT, bool NEXT2>
+__device__ __forceinline__ void stage_mn(bf16* ca, bf16* cb, bf16* na, bf16* nb, int D, const Loader<A_KMAJOR>& la,
+                                       const Loader<B_KMAJOR>& lb, int wave, int wm, int wn, int lane,
+                                       bf16x8 (&fa)[4][4], bf16x8 (&fb)[4][4], f32x16 (&acc)[4][4]) {
+  constexpr int NR = frag_reads<A_KMAJOR, B_KMAJOR>();
+  // s0: part 3 of D+1
+  read_frags<A_KMAJOR, B_KMAJOR>(ca, cb, 2, wm, wn, lane, fa[2], fb[2]);
+  if constexpr (NEXT) lb.template issue<3, 8>(nb, (D + 1) * BK2, wave);
+  mfma_step(fa[0], fb[0], acc);
+  interleave_step<NR, NEXT ? 5 : 0>();
+  __builtin_amdgcn_sched_barrier(0);
+  // s1
+  read_frags<A_KMAJOR, B_KMAJOR>(ca, cb, 3, wm, wn, lane, fa[3], fb[3]);
+  mfma_step(fa[1], fb[1], acc);
+  interleave_step<NR, 0>();
+  __builtin_amdgcn_sched_barrier(0);
+  // s2: barrier, D+1's first fragments, part 1 of D+2
+  if constexpr (NEXT) {
+    stage_barrier<0>();
+    read_frags<A_KMAJOR, B_KMAJOR>(na, nb, 0, wm, wn, lane, fa[0], fb[0]);
+    if constexpr (NEXT2) la.template issue<0, 6>(ca, (D + 2) * BK2, wave);
+  }
+  mfma_step(fa[2], fb[2], acc);
+  interleave_step<NEXT ? NR : 0, NEXT2 ? 6 : 0>();
+  __builtin_amdgcn_sched_barrier(0);
+  // s3: part 2 of D+2
+  if constexpr (NEXT) read_frags<A_KMAJOR, B_KMAJOR>(na, nb, 1, wm, wn, lane, fa[1], fb[1]);
+  if constexpr (NEXT2) {
+    la.template issue<6, 8>(ca, (D + 2) * BK2, wave);
+    lb.template issue<0, 3>(cb, (D + 2) * BK2, wave);
+  }
+  mfma_step(fa[3], fb[3], acc);
+  interleave_step<NEXT ? NR : 0, NEXT2 ? 5 : 0>();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <bool A_KMAJOR, bool B_KMAJOR>
+__device__ __forceinline__ void mainloop_mn(const Operand& A, const Operand& B, int m0, int n0, int nk, bf16* s0,
+                                          bf16* s1, bf16* s2, bf16* s3, f32x16 (&acc)[4][4]) {
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  if (nk <= 0) return;
+  const int nd = nk / 2;
+  const Loader<A_KMAJOR> la(A, m0, wave, lane);
+  const Loader<B_KMAJOR> lb(B, n0, wave, lane);
+  la.template issue<0, 8>(s0, 0, wave);
+  lb.template issue<0, 8>(s1, 0, wave);
+  la.template issue<0, 8>(s2, BK2, wave);
+  lb.template issue<0, 3>(s3, BK2, wave);
+  stage_barrier<11>();
+  bf16x8 fa[4][4], fb[4][4];
+  read_frags<A_KMAJOR, B_KMAJOR>(s0, s1, 0, wm, wn, lane, fa[0], fb[0]);
+  read_frags<A_KMAJOR, B_KMAJOR>(s0, s1, 1, wm, wn, lane, fa[1], fb[1]);
+  int D = 0;
+  for (; D + 2 < nd; D += 2) {
+    stage_mn<A_KMAJOR, B_KMAJOR, true, true>(s0, s1, s2, s3, D, la, lb, wave, wm, wn, lane, fa, fb, acc);
+    stage_mn<A_KMAJOR, B_KMAJOR, true, true>(s2, s3, s0, s1, D + 1, la, lb, wave, wm, wn, lane, fa, fb, acc);
+  }
+  stage_mn<A_KMAJOR, B_KMAJOR, true, false>(s0, s1, s2, s3, D, la, lb, wave, wm, wn, lane, fa, fb, acc);
+  stage_mn<A_KMAJOR, B_KMAJOR, false, false>(s2, s3, s0, s1, D + 1, la, lb, wave, wm, wn, lane, fa, fb, acc);
   stage_barrier<0>();
 }
 
@@ -555,8 +453,8 @@ __device__ __forceinline__ void run_tile(const Operand& A, const Operand& B, con
     if (sch.tok_dim == 3) k_steps = (tv + NST * BK - 1) / (NST * BK) * NST;
   }
   f32x16 acc[4][4];
-  if constexpr (A_KMAJOR && B_KMAJOR) mainloop64(A, B, m0, n0, k_steps, s0, s1, s2, s3, acc);
-  else mainloop<A_KMAJOR, B_KMAJOR>(A, B, m0, n0, k_steps, s0, s1, s2, s3, acc);
+  if constexpr (A_KMAJOR && B_KMAJOR) mainloop_kk(A, B, m0, n0, k_steps, s0, s1, s2, s3, acc);
+  else mainloop_mn<A_KMAJOR, B_KMAJOR>(A, B, m0, n0, k_steps, s0, s1, s2, s3, acc);
   Epi::apply(ep, acc, m0, n0, s0);
 }
 
