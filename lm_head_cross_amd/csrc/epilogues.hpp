@@ -28,6 +28,60 @@ struct Lse {
     float softcap, inv_softcap;
   };
 
+  // Without a softcap: one 32-token column block nb of this wave, (max,
+  // sum exp) over the wave's 128 rows into the exchange buffer, and the
+  // label's logit if a lane's label row is among them.  RAGGED: the tile
+  // straddles Vu.  The two forms are separate instantiations, so the common
+  // one carries no mask and no merge of the 64 values; written as one branchy
+  // body, the register allocator spilled 45 VGPRs per lane here, 370 MB of
+  // scratch traffic per launch at V = 128256.
+  template <bool RAGGED>
+  static __device__ __forceinline__ void column(const Params& p, f32x16 (&acc)[4][4], int nb, int m0, int n0,
+                                                int tv, int wm, int wn, int lane, float* xchg) {
+    const int tc = acc_col(wn, nb, lane);
+    const int t = n0 + tc;
+    const int y_in = p.yc[t];  // t < Tvp: always inside the buffer
+    const int y = t < tv ? y_in : -1;
+    const int row0 = m0 + wm * 128;
+    float zc[64];
+    float mx = kNegInf, lab = 0.0f, found = 0.0f;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float z = acc[mb][nb][r];
+        if constexpr (RAGGED) z = m0 + acc_row(wm, mb, r, lane) < p.vocab_limit ? z : kNegInf;
+        zc[mb * 16 + r] = z;
+        mx = __builtin_fmaxf(mx, z);
+      }
+    const bool in_rows = (unsigned)(y - row0) < 128u;
+    if (__builtin_amdgcn_ballot_w64(in_rows) != 0) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int v = m0 + acc_row(wm, mb, r, lane);
+          lab = v == y ? zc[mb * 16 + r] : lab;
+          found = v == y ? 1.0f : found;
+        }
+    }
+    mx = __builtin_fmaxf(mx, lane_xor32(mx));
+    float s = 0.0f;
+    if (mx != kNegInf) {
+      const float mx2 = mx * kLog2e;
+#pragma unroll
+      for (int i = 0; i < 64; ++i) s += __builtin_amdgcn_exp2f(__builtin_fmaf(zc[i], kLog2e, -mx2));
+    }
+    s += lane_xor32(s);
+    const float lab2 = lane_xor32(lab);
+    const float found2 = lane_xor32(found);
+    if (found2 != 0.0f) { lab = lab2; found = 1.0f; }
+    if (lane < 32) {
+      float* e = xchg + ((wm * 256 + tc) << 2);
+      e[0] = mx; e[1] = s; e[2] = lab; e[3] = found;
+    }
+  }
+
   static __device__ __forceinline__ void apply(const Params& p, f32x16 (&acc)[4][4], int m0, int n0,
                                                bf16* smem) {
     const int lane = threadIdx.x & 63;
@@ -38,65 +92,81 @@ struct Lse {
     const bool ragged = m0 + gemm::BM > p.vocab_limit;
     const int row0 = m0 + wm * 128;   // first head row of this wave's rows
 
+    if constexpr (!CAP) {
+      if (m0 + gemm::BM > p.vocab_limit) {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int tc = acc_col(wn, nb, lane);
-      const int t = n0 + tc;
-      const int y_in = p.yc[t];  // t < Tvp: always inside the buffer
-      const int y = t < tv ? y_in : -1;
-      float zc[64];
-      float mx = kNegInf, lab = 0.0f, found = 0.0f;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float z = acc[mb][nb][r];
-          if constexpr (CAP) z = softcap_apply(z, p.softcap, p.inv_softcap);
-          zc[mb * 16 + r] = z;
+        for (int nb = 0; nb < 4; ++nb) {
+          column<true>(p, acc, nb, m0, n0, tv, wm, wn, lane, xchg);
+          __builtin_amdgcn_sched_barrier(0);
         }
-      // Rows past the usable vocabulary take no part: -inf drops them from
-      // both the max and the sum.  Only the tile that straddles Vu has any.
-      if (ragged) {
+      } else {
 #pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          column<false>(p, acc, nb, m0, n0, tv, wm, wn, lane, xchg);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    } else {
+  #pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int tc = acc_col(wn, nb, lane);
+        const int t = n0 + tc;
+        const int y_in = p.yc[t];  // t < Tvp: always inside the buffer
+        const int y = t < tv ? y_in : -1;
+        float zc[64];
+        float mx = kNegInf, lab = 0.0f, found = 0.0f;
+  #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
+  #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int v = m0 + acc_row(wm, mb, r, lane);
-            zc[mb * 16 + r] = v < p.vocab_limit ? zc[mb * 16 + r] : kNegInf;
+            float z = acc[mb][nb][r];
+            if constexpr (CAP) z = softcap_apply(z, p.softcap, p.inv_softcap);
+            zc[mb * 16 + r] = z;
           }
+        // Rows past the usable vocabulary take no part: -inf drops them from
+        // both the max and the sum.  Only the tile that straddles Vu has any.
+        if (ragged) {
+  #pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int v = m0 + acc_row(wm, mb, r, lane);
+              zc[mb * 16 + r] = v < p.vocab_limit ? zc[mb * 16 + r] : kNegInf;
+            }
+        }
+  #pragma unroll
+        for (int i = 0; i < 64; ++i) mx = __builtin_fmaxf(mx, zc[i]);
+        // The label's logit: looked for only when some lane's label falls in
+        // this wave's 128 rows (about 5% of the time at V = 128256).
+        const bool in_rows = (unsigned)(y - row0) < 128u;
+        if (__builtin_amdgcn_ballot_w64(in_rows) != 0) {
+  #pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int v = m0 + acc_row(wm, mb, r, lane);
+              lab = v == y ? zc[mb * 16 + r] : lab;
+              found = v == y ? 1.0f : found;
+            }
+        }
+        mx = __builtin_fmaxf(mx, lane_xor32(mx));
+        float s = 0.0f;
+        if (mx != kNegInf) {
+          // exp(z - mx) as one fma and the hardware base-2 exponential.
+          const float mx2 = mx * kLog2e;
+  #pragma unroll
+          for (int i = 0; i < 64; ++i) s += __builtin_amdgcn_exp2f(__builtin_fmaf(zc[i], kLog2e, -mx2));
+        }
+        s += lane_xor32(s);
+        const float lab2 = lane_xor32(lab);
+        const float found2 = lane_xor32(found);
+        if (found2 != 0.0f) { lab = lab2; found = 1.0f; }
+        if (lane < 32) {
+          float* e = xchg + ((wm * 256 + tc) << 2);
+          e[0] = mx; e[1] = s; e[2] = lab; e[3] = found;
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int i = 0; i < 64; ++i) mx = __builtin_fmaxf(mx, zc[i]);
-      // The label's logit: looked for only when some lane's label falls in
-      // this wave's 128 rows (about 5% of the time at V = 128256).
-      const bool in_rows = (unsigned)(y - row0) < 128u;
-      if (__builtin_amdgcn_ballot_w64(in_rows) != 0) {
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int v = m0 + acc_row(wm, mb, r, lane);
-            lab = v == y ? zc[mb * 16 + r] : lab;
-            found = v == y ? 1.0f : found;
-          }
-      }
-      mx = __builtin_fmaxf(mx, lane_xor32(mx));
-      float s = 0.0f;
-      if (mx != kNegInf) {
-        // exp(z - mx) as one fma and the hardware base-2 exponential.
-        const float mx2 = mx * kLog2e;
-#pragma unroll
-        for (int i = 0; i < 64; ++i) s += __builtin_amdgcn_exp2f(__builtin_fmaf(zc[i], kLog2e, -mx2));
-      }
-      s += lane_xor32(s);
-      const float lab2 = lane_xor32(lab);
-      const float found2 = lane_xor32(found);
-      if (found2 != 0.0f) { lab = lab2; found = 1.0f; }
-      if (lane < 32) {
-        float* e = xchg + ((wm * 256 + tc) << 2);
-        e[0] = mx; e[1] = s; e[2] = lab; e[3] = found;
-      }
-      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
     // Waves of the top row merge the bottom row's pairs and write out.
