@@ -42,6 +42,7 @@ namespace gemm {
 
 constexpr int BM = 256;
 constexpr int BN = 256;
+static_assert(BM == BN, "token tiles are BM wide along M and N alike");
 constexpr int BK = 32;                        // K is counted in steps of 32 (Schedule::k_steps) ...
 constexpr int NST = 4;                        // ... and padded to a multiple of NST steps (128)
 constexpr int BK2 = 64;                       // k per LDS stage
@@ -441,17 +442,26 @@ template <bool A_KMAJOR, bool B_KMAJOR, class Epi>
 __device__ __forceinline__ void run_tile(const Operand& A, const Operand& B, const Schedule& sch,
                                          const typename Epi::Params& ep, int pid, bf16* s0, bf16* s1, bf16* s2,
                                          bf16* s3) {
-  int tm, tn;
-  tile_of(pid, sch.tiles_m, sch.tiles_n, tm, tn);
-  const int m0 = tm * BM;
-  const int n0 = tn * BN;
+  // With tokens along M or N, the grid covers every token tile the host
+  // allows for, but only ceil(Tv / 256) of them hold valid tokens (Tv is
+  // read on the device).  The workgroup ids are mapped onto those tiles
+  // alone and the rest exit: mapped over the full grid, the tiles past Tv
+  // took whole XCDs' shares (tile_of gives each XCD a contiguous run), and
+  // at half the tokens ignored half the XCDs sat idle in dH.
+  int tiles_m = sch.tiles_m, tiles_n = sch.tiles_n;
   int k_steps = sch.k_steps;
   if (sch.tok_dim != 0) {
     const int tv = *sch.tok_count;
-    if (sch.tok_dim == 1 && m0 >= tv) return;
-    if (sch.tok_dim == 2 && n0 >= tv) return;
+    const int tok_tiles = (tv + BM - 1) / BM;
+    if (sch.tok_dim == 1) tiles_m = min(tiles_m, tok_tiles);
+    if (sch.tok_dim == 2) tiles_n = min(tiles_n, tok_tiles);
     if (sch.tok_dim == 3) k_steps = (tv + NST * BK - 1) / (NST * BK) * NST;
+    if (pid >= tiles_m * tiles_n) return;
   }
+  int tm, tn;
+  tile_of(pid, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM;
+  const int n0 = tn * BN;
   f32x16 acc[4][4];
   if constexpr (A_KMAJOR && B_KMAJOR) mainloop_kk(A, B, m0, n0, k_steps, s0, s1, s2, s3, acc);
   else mainloop_mn<A_KMAJOR, B_KMAJOR>(A, B, m0, n0, k_steps, s0, s1, s2, s3, acc);
