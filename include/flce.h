@@ -81,7 +81,12 @@ typedef enum flce_dtype {
  * Problem description, shared by every entry point.
  *
  * num_tokens        T >= 0: flattened [batch, sequence] positions.
- * hidden            H > 0, a multiple of 128.
+ * hidden            H > 0, a multiple of 8 (rows of 16-byte pieces).  The
+ *                   kernels step through H in groups of 128: when H is not a
+ *                   multiple of 128, each call copies the head's rows < Vu
+ *                   into the workspace with zero-padded rows of Hp =
+ *                   ceil(H/128)*128 elements (Vu*Hp*2 more bytes), and the
+ *                   gathered hidden rows are padded the same way.
  * vocab             V: rows of the head, padding included.
  * unpadded_vocab    Vu, 0 < Vu <= V: rows that take part in the softmax
  *                   (Inkling2 page, constructor argument unpadded_vocab_size).
@@ -96,7 +101,7 @@ typedef enum flce_dtype {
  *                   each call rounds to bf16 itself (Inkling2 page, class
  *                   description: an FP32 head is rounded to BF16, the cast
  *                   FSDP applies).  The rounded copy of rows < Vu is staged
- *                   in the workspace, which grows by Vu*H*2 bytes; rows >= Vu
+ *                   in the workspace, which grows by Vu*Hp*2 bytes; rows >= Vu
  *                   are never read.
  */
 typedef struct flce_problem {

@@ -73,18 +73,21 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(const int64_t* __re
   }
 }
 
-// Xc[t, :] = X[valid_idx[t], :] for t < Tv, 0 for Tv <= t < Tvp.
-__global__ __launch_bounds__(256) void k_gather(const uint4* __restrict__ X, int64_t row_vec,
+// Xc[t, :H] = X[valid_idx[t], :] for t < Tv; every other element of the
+// Tvp x Hp buffer (rows Tv..Tvp, columns H..Hp) is 0.  Rows are moved in
+// 16-byte pieces: in_vec = H/8 of them per input row, out_vec = Hp/8 per
+// output row.
+__global__ __launch_bounds__(256) void k_gather(const uint4* __restrict__ X, int64_t in_vec, int64_t out_vec,
                                                  const int32_t* __restrict__ valid_idx, const Meta* meta,
                                                  uint4* __restrict__ Xc, int64_t Tvp) {
   const int tv = meta->n_valid;
-  const int64_t total = Tvp * row_vec;
+  const int64_t total = Tvp * out_vec;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t t = i / row_vec;
-    const int64_t c = i - t * row_vec;
+    const int64_t t = i / out_vec;
+    const int64_t c = i - t * out_vec;
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (t < tv) v = X[(int64_t)valid_idx[t] * row_vec + c];
+    if (t < tv && c < in_vec) v = X[(int64_t)valid_idx[t] * in_vec + c];
     Xc[i] = v;
   }
 }
@@ -210,6 +213,36 @@ __global__ __launch_bounds__(256) void k_round_bf16(const float* __restrict__ sr
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = (bf16)src[i];
 }
 
+// Rows < `rows` of a head [*, H] into a bf16 copy [rows, Hp] whose columns
+// H..Hp are 0: an fp32 head is rounded to nearest even, a bf16 head copied.
+// H is a multiple of 8, so each 16-byte output piece lies wholly inside or
+// wholly past the end of its source row.
+template <class Src>
+__global__ __launch_bounds__(256) void k_stage_head(const Src* __restrict__ src, int64_t H, int64_t Hp,
+                                                     int64_t rows, uint4* __restrict__ dst) {
+  const int64_t vec = Hp / 8;
+  const int64_t n = rows * vec;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) {
+    const int64_t r = i / vec;
+    const int64_t c = (i - r * vec) * 8;
+    uint4 o = make_uint4(0, 0, 0, 0);
+    if (c < H) {
+      if constexpr (sizeof(Src) == 4) {
+        const float4 a = *reinterpret_cast<const float4*>(src + r * H + c);
+        const float4 b = *reinterpret_cast<const float4*>(src + r * H + c + 4);
+        bf16x8 v;
+        v[0] = (bf16)a.x; v[1] = (bf16)a.y; v[2] = (bf16)a.z; v[3] = (bf16)a.w;
+        v[4] = (bf16)b.x; v[5] = (bf16)b.y; v[6] = (bf16)b.z; v[7] = (bf16)b.w;
+        o = *reinterpret_cast<const uint4*>(&v);
+      } else {
+        o = *reinterpret_cast<const uint4*>(src + r * H + c);
+      }
+    }
+    dst[i] = o;
+  }
+}
+
 __global__ __launch_bounds__(256) void k_round_bf16_vec(const float4* __restrict__ src, bf16x4* __restrict__ dst,
                                                          int64_t n4) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -240,6 +273,8 @@ constexpr size_t kAlign = 256;
 // Sizes derived from a validated problem.
 struct Plan {
   int64_t T, H, V, Vu;
+  int64_t Hp;           // H rounded up to 128: the row length of Xc, XcT's row count and a staged head's rows
+  bool stage_head;      // the kernels read a bf16 copy of the head's rows < Vu (fp32 head, or H != Hp)
   int64_t Tvp;          // T rounded up to 256 (the token tile)
   int64_t tiles_t;      // Tvp / 256
   int64_t tiles_v;      // ceil(Vu / 256): forward vocab tiles
@@ -248,7 +283,7 @@ struct Plan {
   int64_t nchunks;
   // workspace byte offsets
   size_t off_meta, off_valid, off_yc, off_label, off_scale, off_bsum, off_xc;
-  size_t off_wst;       // bf16 staging of an fp32 head's rows < Vu (0 bytes for a bf16 head)
+  size_t off_wst;       // the staged head [Vu, Hp] bf16 (0 bytes when the caller's head is read directly)
   size_t off_part;      // forward region
   size_t off_g, off_hacc, off_xct;  // backward region
   size_t total;
@@ -262,7 +297,7 @@ int validate(const flce_problem_t* p) {
   if (p->reduction != FLCE_REDUCTION_SUM && p->reduction != FLCE_REDUCTION_MEAN) return FLCE_ERR_INVALID_ARG;
   if (p->num_label_tokens == 0) return FLCE_ERR_INVALID_ARG;
   if (p->weight_dtype != FLCE_DTYPE_BF16 && p->weight_dtype != FLCE_DTYPE_FP32) return FLCE_ERR_UNSUPPORTED;
-  if (p->hidden % 128 != 0) return FLCE_ERR_UNSUPPORTED;
+  if (p->hidden % 8 != 0) return FLCE_ERR_UNSUPPORTED;
   // 32-bit token / row / column indices inside the kernels.
   if (p->num_tokens > (int64_t(1) << 30) || p->vocab > (int64_t(1) << 30) || p->hidden > (int64_t(1) << 20))
     return FLCE_ERR_UNSUPPORTED;
@@ -318,6 +353,8 @@ Plan make_plan(const flce_problem_t* p, int n_cu = 256) {
   pl.H = p->hidden;
   pl.V = p->vocab;
   pl.Vu = p->unpadded_vocab;
+  pl.Hp = align_up((size_t)pl.H, 128);
+  pl.stage_head = p->weight_dtype == FLCE_DTYPE_FP32 || pl.Hp != pl.H;
   pl.Tvp = align_up((size_t)pl.T, 256);
   pl.tiles_t = pl.Tvp / 256;
   pl.tiles_v = ceil_div(pl.Vu, 256);
@@ -327,7 +364,7 @@ Plan make_plan(const flce_problem_t* p, int n_cu = 256) {
   // sized for the widest chunk, so the workspace does not depend on the
   // device.
   const int64_t ct_max = std::max<int64_t>(1, pl.Vu / 1024);
-  const int64_t ct = pick_chunk_tiles(pl.tiles_v, pl.tiles_t, pl.tiles_h, pl.H, pl.Tvp, ct_max, n_cu);
+  const int64_t ct = pick_chunk_tiles(pl.tiles_v, pl.tiles_t, pl.tiles_h, pl.Hp, pl.Tvp, ct_max, n_cu);
   pl.vc = ct * 256;
   pl.nchunks = ceil_div(pl.tiles_v, ct);
 
@@ -339,9 +376,10 @@ Plan make_plan(const flce_problem_t* p, int n_cu = 256) {
   pl.off_label = take(pl.Tvp * 4);
   pl.off_scale = take(16);
   pl.off_bsum = take(pl.Tvp / kCombineTokens * 8);
-  pl.off_xc = take(pl.Tvp * pl.H * 2);
-  // An fp32 head: the bf16 copy of its usable rows, staged here by each call.
-  pl.off_wst = take(p->weight_dtype == FLCE_DTYPE_FP32 ? pl.Vu * pl.H * 2 : 0);
+  pl.off_xc = take(pl.Tvp * pl.Hp * 2);
+  // An fp32 head, or rows not a multiple of 128 long: the bf16 copy of its
+  // usable rows, staged here by each call.
+  pl.off_wst = take(pl.stage_head ? pl.Vu * pl.Hp * 2 : 0);
   const size_t common = o;
   pl.off_part = take(pl.tiles_v * pl.Tvp * 8);
   const size_t fwd_end = o;
@@ -349,7 +387,7 @@ Plan make_plan(const flce_problem_t* p, int n_cu = 256) {
   pl.off_g = take(pl.Tvp * ct_max * 256 * 2);
   // Every chunk width below tiles_v gives more than one chunk.
   pl.off_hacc = take(pl.tiles_v > 1 ? pl.Tvp * pl.H * 4 : 0);
-  pl.off_xct = take(pl.Tvp * pl.H * 2);
+  pl.off_xct = take(pl.Tvp * pl.Hp * 2);
   const size_t bwd_end = o;
   pl.total = std::max(fwd_end, bwd_end);
   return pl;
@@ -378,19 +416,28 @@ void zero_fill(void* p, int64_t bytes, hipStream_t s) {
   hipLaunchKernelGGL(k_zero, dim3(grid_for(n16, 256, 8192)), dim3(256), 0, s, (uint4*)p, n16);
 }
 
-// The bf16 head the kernels read: the caller's for a bf16 head; for an fp32
-// head its rows < Vu rounded to nearest even into the workspace ("nemo_
-// automodel.components.models.inkling2.loss", class description: an fp32
-// head is rounded to bf16 with the cast FSDP applies).  Rows >= Vu are never
-// read.
+// The bf16 head the kernels read, rows of Hp elements: the caller's for a
+// bf16 head with H a multiple of 128; otherwise its rows < Vu copied into
+// the workspace, an fp32 head rounded to nearest even ("nemo_automodel.
+// components.models.inkling2.loss", class description: an fp32 head is
+// rounded to bf16 with the cast FSDP applies), with zero columns H..Hp.
+// Rows >= Vu are never read.
 const bf16* staged_head(const Plan& pl, const flce_problem_t& p, const void* weight, void* workspace,
                         hipStream_t stream) {
-  if (p.weight_dtype == FLCE_DTYPE_BF16) return static_cast<const bf16*>(weight);
+  if (!pl.stage_head) return static_cast<const bf16*>(weight);
   bf16* wst = ws_at<bf16>(workspace, pl.off_wst);
-  const int64_t n4 = pl.Vu * pl.H / 4;  // H is a multiple of 128
   TraceScope tr(FLCE_KERNEL_AUX, 0.0, stream);
-  hipLaunchKernelGGL(k_round_bf16_vec, dim3(grid_for(n4, 256, 16384)), dim3(256), 0, stream,
-                     static_cast<const float4*>(weight), reinterpret_cast<bf16x4*>(wst), n4);
+  if (pl.Hp == pl.H) {
+    const int64_t n4 = pl.Vu * pl.H / 4;
+    hipLaunchKernelGGL(k_round_bf16_vec, dim3(grid_for(n4, 256, 16384)), dim3(256), 0, stream,
+                       static_cast<const float4*>(weight), reinterpret_cast<bf16x4*>(wst), n4);
+  } else if (p.weight_dtype == FLCE_DTYPE_FP32) {
+    hipLaunchKernelGGL(k_stage_head<float>, dim3(grid_for(pl.Vu * pl.Hp / 8, 256, 16384)), dim3(256), 0,
+                       stream, static_cast<const float*>(weight), pl.H, pl.Hp, pl.Vu, reinterpret_cast<uint4*>(wst));
+  } else {
+    hipLaunchKernelGGL(k_stage_head<bf16>, dim3(grid_for(pl.Vu * pl.Hp / 8, 256, 16384)), dim3(256), 0,
+                       stream, static_cast<const bf16*>(weight), pl.H, pl.Hp, pl.Vu, reinterpret_cast<uint4*>(wst));
+  }
   return wst;
 }
 
@@ -402,11 +449,11 @@ void launch_compact_gather(const Plan& pl, const flce_problem_t& p, const int64_
     hipLaunchKernelGGL(k_compact, dim3(1), dim3(kCompactThreads), 0, stream, labels, (int)pl.T, (int)pl.Vu,
                        p.ignore_index, meta, valid_idx, yc, device_status, lse, token_loss);
   }
-  const int64_t row_vec = pl.H / 8;
+  const int64_t in_vec = pl.H / 8, out_vec = pl.Hp / 8;
   TraceScope tr(FLCE_KERNEL_GATHER, 0.0, stream);
-  hipLaunchKernelGGL(k_gather, dim3(grid_for(pl.Tvp * row_vec, 256, 16384)), dim3(256), 0, stream,
-                     (const uint4*)hidden, row_vec, (const int32_t*)valid_idx, (const Meta*)meta, (uint4*)xc,
-                     pl.Tvp);
+  hipLaunchKernelGGL(k_gather, dim3(grid_for(pl.Tvp * out_vec, 256, 16384)), dim3(256), 0, stream,
+                     (const uint4*)hidden, in_vec, out_vec, (const int32_t*)valid_idx, (const Meta*)meta,
+                     (uint4*)xc, pl.Tvp);
 }
 
 }  // namespace
@@ -484,9 +531,9 @@ int flce_forward(const flce_problem_t* problem, const void* hidden, const void* 
   const bf16* Wb = staged_head(pl, p, weight, workspace, stream);
   launch_compact_gather(pl, p, labels, hidden, meta, valid_idx, yc, device_status, lse, token_loss, xc, stream);
   {
-    gemm::Operand A{Wb, pl.H, (int)pl.Vu - 1, 0};
-    gemm::Operand B{xc, pl.H, (int)pl.Tvp - 1, 0};
-    gemm::Schedule sch{(int)pl.tiles_v, (int)pl.tiles_t, k_steps_for(pl.H), tv, 2};
+    gemm::Operand A{Wb, pl.Hp, (int)pl.Vu - 1, 0};
+    gemm::Operand B{xc, pl.Hp, (int)pl.Tvp - 1, 0};
+    gemm::Schedule sch{(int)pl.tiles_v, (int)pl.tiles_t, k_steps_for(pl.Hp), tv, 2};
     const dim3 grid(pl.tiles_v * pl.tiles_t);
     TraceScope tr(FLCE_KERNEL_PROJ_LSE, 2.0 * pl.T * pl.Vu * pl.H, stream);
     if (p.softcap > 0.0f) {
@@ -547,8 +594,8 @@ int flce_backward(const flce_problem_t* problem, const void* hidden, const void*
   bf16* xct = ws_at<bf16>(workspace, pl.off_xct);
   {
     TraceScope tr(FLCE_KERNEL_GATHER, 0.0, stream);
-    hipLaunchKernelGGL(k_transpose_xc, dim3((unsigned)(pl.Tvp / 64), (unsigned)(pl.H / 64)), dim3(256), 0, stream,
-                       (const bf16*)xc, pl.H, pl.Tvp, xct);
+    hipLaunchKernelGGL(k_transpose_xc, dim3((unsigned)(pl.Tvp / 64), (unsigned)(pl.Hp / 64)), dim3(256), 0,
+                       stream, (const bf16*)xc, pl.Hp, pl.Tvp, xct);
   }
   {
     TraceScope tr(FLCE_KERNEL_AUX, 0.0, stream);
@@ -563,14 +610,14 @@ int flce_backward(const flce_problem_t* problem, const void* hidden, const void*
     const int64_t v0 = c * pl.vc;
     const int64_t vw = std::min(pl.vc, pl.Vu - v0);
     const int64_t tiles_c = ceil_div(vw, 256);
-    const bf16* Wc = W + v0 * pl.H;
+    const bf16* Wc = W + v0 * pl.Hp;
     const double chunk_flops = 2.0 * pl.T * vw * pl.H;
 
     // 1. logits of the chunk -> G (bf16, token-major)
     {
-      gemm::Operand A{Wc, pl.H, (int)vw - 1, 0};
-      gemm::Operand B{xc, pl.H, (int)pl.Tvp - 1, 0};
-      gemm::Schedule sch{(int)tiles_c, (int)pl.tiles_t, k_steps_for(pl.H), tv, 2};
+      gemm::Operand A{Wc, pl.Hp, (int)vw - 1, 0};
+      gemm::Operand B{xc, pl.Hp, (int)pl.Tvp - 1, 0};
+      gemm::Schedule sch{(int)tiles_c, (int)pl.tiles_t, k_steps_for(pl.Hp), tv, 2};
       const dim3 grid(tiles_c * pl.tiles_t);
       TraceScope tr(FLCE_KERNEL_RECOMPUTE_G, chunk_flops, stream);
       if (p.softcap > 0.0f) {
@@ -589,7 +636,7 @@ int flce_backward(const flce_problem_t* problem, const void* hidden, const void*
     //    dW reads G MN-major (transposing LDS reads) and Xc K-major from XcT.
     {
       gemm::Operand Ah{G, pl.vc, (int)pl.Tvp - 1, 0};
-      gemm::Operand Bh{Wc, pl.H, (int)pl.H - 1, (int)vw - 1};
+      gemm::Operand Bh{Wc, pl.Hp, (int)pl.H - 1, (int)vw - 1};
       gemm::Schedule sh{(int)pl.tiles_t, (int)pl.tiles_h, k_steps_for(vw), tv, 1};
       int mode = 0;
       if (c == 0) mode |= epi::kAccFirst;

@@ -81,6 +81,19 @@ def test_fp32_head_workspace_holds_the_staged_rows():
     assert b[1] - a[1] == 256000 * 3072 * 2  # bf16 copy of the usable rows only
 
 
+def test_unaligned_hidden_stages_a_padded_head():
+    """H a multiple of 8 but not of 128: the head's usable rows are staged
+    with rows of Hp = ceil(H/128)*128 elements; the fp32 accumulator of dH
+    keeps rows of H.  Against the same problem at H = Hp (nothing staged):"""
+    T, V, H, Hp = 4096, 201088, 2880, 2944
+    a = _ws(make_problem(T, H, V))
+    b = _ws(make_problem(T, Hp, V))
+    assert a[0] == b[0] == _lib.FLCE_OK
+    assert a[1] - b[1] == V * Hp * 2 - T * (Hp - H) * 4
+    for h in (8, 136, 200, 1600):
+        assert _ws(make_problem(64, h, 1000))[0] == _lib.FLCE_OK
+
+
 def test_library_source_allocates_no_device_memory():
     """The caller owns every buffer: no allocation or free call in the HIP
     sources (the workspace comes in as an argument)."""
@@ -104,7 +117,8 @@ def test_library_source_allocates_no_device_memory():
     (dict(reduction=2), _lib.FLCE_ERR_INVALID_ARG),
     (dict(num_label_tokens=0), _lib.FLCE_ERR_INVALID_ARG),
     (dict(hidden=100), _lib.FLCE_ERR_UNSUPPORTED),
-    (dict(hidden=192), _lib.FLCE_ERR_UNSUPPORTED),
+    (dict(hidden=12), _lib.FLCE_ERR_UNSUPPORTED),
+    (dict(hidden=4100), _lib.FLCE_ERR_UNSUPPORTED),
     (dict(weight_dtype=7), _lib.FLCE_ERR_UNSUPPORTED),
 ])
 def test_invalid_problem_rejected(kw, expect):

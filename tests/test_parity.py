@@ -39,6 +39,11 @@ SMALL = {
                      labels="argmax70"),
     "fp32_head": _small(105, T=513, H=128, V=1536, Vu=1500, w_std=0.2, head_fp32=True, softcap=30.0,
                         ignore_frac=0.05),
+    # H a multiple of 8 but not of 128: rows padded to 128-wide groups
+    "hidden_200": _small(106, T=530, H=200, V=1800, Vu=1750, w_std=0.1, ignore_frac=0.1),
+    "hidden_328_fp32_head": _small(107, T=300, H=328, V=1100, Vu=1100, w_std=0.1, head_fp32=True,
+                                   softcap=30.0, ignore_frac=0.05),
+    "hidden_8": _small(108, T=70, H=8, V=300, Vu=290, w_std=1.0, reduction="mean", ignore_frac=0.1),
 }
 
 
@@ -102,6 +107,32 @@ def test_padding_rows_never_read():
     for k in ("lse", "token_loss", "dX", "dW"):
         assert torch.equal(a[k], b[k]), k
     assert torch.all(b["dW"][inp["unpadded_vocab"]:] == 0)
+
+
+@pytest.mark.parametrize("name", ["hidden_200", "hidden_328_fp32_head"])
+def test_unaligned_hidden_equals_zero_padded_problem(name):
+    """H not a multiple of 128 gives, bit for bit, the results of the same
+    problem with X and W extended by zero columns to the next multiple of 128
+    (the padded problem's extra dX and dW columns are exactly 0); with the
+    fp32 head handed over directly, the staging kernel's rounding is the
+    rounding kernel's."""
+    w = SMALL[name]
+    inp = make_inputs(w)
+    H = w.H
+    Hp = (H + 127) // 128 * 128
+    direct = inp["weight"].dtype == torch.float32
+    a = run_hip(inp, fp32_head_direct=direct)
+    padded = dict(inp)
+    padded["hidden"] = torch.nn.functional.pad(inp["hidden"], (0, Hp - H))
+    padded["weight"] = torch.nn.functional.pad(inp["weight"], (0, Hp - H))
+    b = run_hip(padded)
+    assert a["status"] == b["status"] == 0
+    assert a["loss"] == b["loss"]
+    for k in ("lse", "token_loss"):
+        assert torch.equal(a[k], b[k]), k
+    assert torch.equal(a["dX"], b["dX"][:, :H])
+    assert torch.equal(a["dW"], b["dW"][:, :H])
+    assert torch.all(b["dX"][:, H:] == 0) and torch.all(b["dW"][:, H:] == 0)
 
 
 def _custom(inp, labels, **kw):
