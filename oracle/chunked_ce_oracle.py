@@ -29,7 +29,7 @@ given logits (bf16 and fp32 values are exact in float64).  The log-sum-exp,
 the softmax-minus-onehot and the normaliser are the fused linear oracle's own
 definitions (those of the main page's loss), applied to the logits as given.
 
-Readings of points the page leaves open (each is listed in the design doc):
+Readings of points the page leaves open:
 
 * reductions 'sum' and 'mean', and ``num_label_tokens`` dividing either, as
   for the fused linear loss;

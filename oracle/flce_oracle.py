@@ -26,7 +26,7 @@ float64 rounding.  The only blocking is over token rows (and, for dW rows,
 over vocab rows), which bounds memory; each token's value is still computed
 from its own definition.  A library matmul serves as the projection step.
 
-Readings of points the pages leave open (each is listed in the design doc):
+Readings of points the pages leave open:
 
 * softcap: z' = c * tanh(z / c) for c > 0; c = 0 turns it off; c < 0 is an
   error.  Its derivative is 1 - (z'/c)^2.
