@@ -81,6 +81,9 @@ typedef enum flce_dtype {
  * Problem description, shared by every entry point.
  *
  * num_tokens        T >= 0: flattened [batch, sequence] positions.
+ *                   Sizes beyond T = 2^21, V = 2^23 or H = 2^20 return
+ *                   FLCE_ERR_UNSUPPORTED (the kernels address a 256-row
+ *                   tile of any operand with 32-bit byte offsets).
  * hidden            H > 0, a multiple of 8 (rows of 16-byte pieces).  The
  *                   kernels step through H in groups of 128: when H is not a
  *                   multiple of 128, each call copies the head's rows < Vu

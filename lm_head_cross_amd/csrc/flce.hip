@@ -298,8 +298,12 @@ int validate(const flce_problem_t* p) {
   if (p->num_label_tokens == 0) return FLCE_ERR_INVALID_ARG;
   if (p->weight_dtype != FLCE_DTYPE_BF16 && p->weight_dtype != FLCE_DTYPE_FP32) return FLCE_ERR_UNSUPPORTED;
   if (p->hidden % 8 != 0) return FLCE_ERR_UNSUPPORTED;
-  // 32-bit token / row / column indices inside the kernels.
-  if (p->num_tokens > (int64_t(1) << 30) || p->vocab > (int64_t(1) << 30) || p->hidden > (int64_t(1) << 20))
+  // The GEMM loaders address a 256-row tile with 32-bit byte offsets from a
+  // buffer resource of under 2 GB: 256 rows of ld bf16 elements must stay
+  // below 2^31 bytes for every row length the kernels use (Hp, the padded
+  // token count, and the chunk width, at most V/4).  These bounds keep each
+  // at or below 2^30 bytes, and every tile count within an int.
+  if (p->num_tokens > (int64_t(1) << 21) || p->vocab > (int64_t(1) << 23) || p->hidden > (int64_t(1) << 20))
     return FLCE_ERR_UNSUPPORTED;
   return FLCE_OK;
 }

@@ -94,6 +94,11 @@ def test_unaligned_hidden_stages_a_padded_head():
         assert _ws(make_problem(64, h, 1000))[0] == _lib.FLCE_OK
 
 
+def test_largest_accepted_sizes():
+    for T, H, V in ((1 << 21, 4096, 128256), (4096, 4096, 1 << 23), (256, 1 << 20, 1024)):
+        assert _ws(make_problem(T, H, V))[0] == _lib.FLCE_OK, (T, H, V)
+
+
 def test_library_source_allocates_no_device_memory():
     """The caller owns every buffer: no allocation or free call in the HIP
     sources (the workspace comes in as an argument)."""
@@ -120,6 +125,10 @@ def test_library_source_allocates_no_device_memory():
     (dict(hidden=12), _lib.FLCE_ERR_UNSUPPORTED),
     (dict(hidden=4100), _lib.FLCE_ERR_UNSUPPORTED),
     (dict(weight_dtype=7), _lib.FLCE_ERR_UNSUPPORTED),
+    # 32-bit tile offsets: beyond these sizes the call is refused
+    (dict(num_tokens=(1 << 21) + 1), _lib.FLCE_ERR_UNSUPPORTED),
+    (dict(vocab=(1 << 23) + 8, unpadded_vocab=1000), _lib.FLCE_ERR_UNSUPPORTED),
+    (dict(hidden=(1 << 20) + 8), _lib.FLCE_ERR_UNSUPPORTED),
 ])
 def test_invalid_problem_rejected(kw, expect):
     p = make_problem(64, 128, 1000)
