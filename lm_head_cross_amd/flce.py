@@ -255,19 +255,25 @@ class FusedLinearCrossEntropy(torch.nn.Module):
     Mirrors the constructor (ignore_index, logit_softcapping, reduction) and
     ``forward`` (hidden_states, labels, lm_weight, num_label_tokens,
     grad_reduce_group) of the linear_ce page; the loss is a scalar on the
-    device of ``hidden_states``.
+    device of ``hidden_states``.  ``unpadded_vocab_size`` (None: every head
+    row) restricts the softmax to the first rows, as on the Inkling2 page.
+    The head's gradient is computed in fp32 and handed to autograd, which
+    gives a bf16 head a bf16 gradient and an fp32 head the fp32 one.
     """
 
-    def __init__(self, ignore_index: int = -100, logit_softcapping: float = 0, reduction: str = "sum"):
+    def __init__(self, ignore_index: int = -100, logit_softcapping: float = 0, reduction: str = "sum",
+                 unpadded_vocab_size: int | None = None):
         super().__init__()
         if reduction not in _REDUCTIONS:
             raise ValueError(f"reduction must be one of {sorted(_REDUCTIONS)}")
         if logit_softcapping < 0:
             raise ValueError("logit_softcapping must be >= 0")
+        if unpadded_vocab_size is not None and unpadded_vocab_size <= 0:
+            raise ValueError("unpadded_vocab_size must be positive")
         self.ignore_index = ignore_index
         self.logit_softcapping = logit_softcapping
         self.reduction = reduction
-        self.unpadded_vocab_size = None
+        self.unpadded_vocab_size = None if unpadded_vocab_size is None else int(unpadded_vocab_size)
 
     @staticmethod
     def materialize_lm_weight(lm_weight, grad_reduce_group=None):
@@ -293,7 +299,6 @@ class Inkling2FusedLinearCrossEntropy(FusedLinearCrossEntropy):
 
     def __init__(self, unpadded_vocab_size: int, logit_softcapping: float = 30.0, ignore_index: int = -100,
                  reduction: str = "sum"):
-        super().__init__(ignore_index, logit_softcapping, reduction)
-        if unpadded_vocab_size <= 0:
-            raise ValueError("unpadded_vocab_size must be positive")
-        self.unpadded_vocab_size = int(unpadded_vocab_size)
+        if unpadded_vocab_size is None:
+            raise ValueError("unpadded_vocab_size is required")
+        super().__init__(ignore_index, logit_softcapping, reduction, unpadded_vocab_size)
