@@ -16,7 +16,11 @@ using gemm::acc_row;
 // token's label also records z'[t, y_t].  (Inkling2 loss page, class
 // description: softcap and cross entropy in fp32, rows past the usable
 // vocabulary never enter the softmax.)
-template <bool CAP>
+//
+// MB: MFMA blocks per wave along the head rows (4 for the 256-row tile, 6
+// for the 384-row one); the waves' two rows of 32*MB head rows are merged
+// through LDS at the end.
+template <bool CAP, int MB = 4>
 struct Lse {
   struct Params {
     float2* partials;       // [tiles_v][ldp]
@@ -27,151 +31,96 @@ struct Lse {
     int vocab_limit;        // Vu
     float softcap, inv_softcap;
   };
+  static constexpr int kWaveRows = 32 * MB;
+  static constexpr int kTileRows = 2 * kWaveRows;
 
-  // Without a softcap: one 32-token column block nb of this wave, (max,
-  // sum exp) over the wave's 128 rows into the exchange buffer, and the
-  // label's logit if a lane's label row is among them.  RAGGED: the tile
-  // straddles Vu.  The two forms are separate instantiations, so the common
-  // one carries no mask and no merge of the 64 values; written as one branchy
-  // body, the register allocator spilled 45 VGPRs per lane here, 370 MB of
-  // scratch traffic per launch at V = 128256.
-  template <bool RAGGED>
-  static __device__ __forceinline__ void column(const Params& p, f32x16 (&acc)[4][4], int nb, int m0, int n0,
-                                                int tv, int wm, int wn, int lane, float* xchg) {
-    const int tc = acc_col(wn, nb, lane);
-    const int t = n0 + tc;
-    const int y_in = p.yc[t];  // t < Tvp: always inside the buffer
-    const int y = t < tv ? y_in : -1;
-    const int row0 = m0 + wm * 128;
-    float zc[64];
-    float mx = kNegInf, lab = 0.0f, found = 0.0f;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float z = acc[mb][nb][r];
-        if constexpr (RAGGED) z = m0 + acc_row(wm, mb, r, lane) < p.vocab_limit ? z : kNegInf;
-        zc[mb * 16 + r] = z;
-        mx = __builtin_fmaxf(mx, z);
-      }
-    const bool in_rows = (unsigned)(y - row0) < 128u;
-    if (__builtin_amdgcn_ballot_w64(in_rows) != 0) {
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int v = m0 + acc_row(wm, mb, r, lane);
-          lab = v == y ? zc[mb * 16 + r] : lab;
-          found = v == y ? 1.0f : found;
-        }
-    }
-    mx = __builtin_fmaxf(mx, lane_xor32(mx));
-    float s = 0.0f;
-    if (mx != kNegInf) {
-      const float mx2 = mx * kLog2e;
-#pragma unroll
-      for (int i = 0; i < 64; ++i) s += __builtin_amdgcn_exp2f(__builtin_fmaf(zc[i], kLog2e, -mx2));
-    }
-    s += lane_xor32(s);
-    const float lab2 = lane_xor32(lab);
-    const float found2 = lane_xor32(found);
-    if (found2 != 0.0f) { lab = lab2; found = 1.0f; }
-    if (lane < 32) {
-      float* e = xchg + ((wm * 256 + tc) << 2);
-      e[0] = mx; e[1] = s; e[2] = lab; e[3] = found;
-    }
+  static __device__ __forceinline__ void apply(const Params& p, f32x16 (&acc)[MB][4], int m0, int n0,
+                                               bf16* smem) {
+    apply(p, acc, m0, m0, n0, smem);
   }
 
-  static __device__ __forceinline__ void apply(const Params& p, f32x16 (&acc)[4][4], int m0, int n0,
+  // m0: the tile's first head row (its partials slot is m0 / kTileRows);
+  // a0 <= m0: the head row of accumulator row 0.  Rows outside [m0, Vu) are
+  // dropped: past Vu they are not in the softmax, below m0 (a last tile
+  // computed shifted down) they belong to the tile before.
+  //
+  // Per lane and token column, the 16 values of one MFMA block at a time:
+  // the running (max, sum) pair takes each block with one rescale, which
+  // keeps a block's 16 values the only temporaries.
+  static __device__ __forceinline__ void apply(const Params& p, f32x16 (&acc)[MB][4], int m0, int a0, int n0,
                                                bf16* smem) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int tv = *p.tok_count;
     float* xchg = reinterpret_cast<float*>(smem);  // [2][256][4]
-    const bool ragged = m0 + gemm::BM > p.vocab_limit;
-    const int row0 = m0 + wm * 128;   // first head row of this wave's rows
-
-    if constexpr (!CAP) {
-      if (m0 + gemm::BM > p.vocab_limit) {
+    const bool ragged = a0 < m0 || a0 + kTileRows > p.vocab_limit;
+    const int row0 = a0 + wm * kWaveRows;   // head row of this wave's first accumulator row
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          column<true>(p, acc, nb, m0, n0, tv, wm, wn, lane, xchg);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      } else {
+    for (int nb = 0; nb < 4; ++nb) {
+      const int tc = acc_col(wn, nb, lane);
+      const int t = n0 + tc;
+      const int y_in = p.yc[t];  // t < Tvp: always inside the buffer
+      const int y = t < tv ? y_in : -1;
+      // The label's logit is looked for only when some lane's label falls in
+      // this wave's rows (about 5% of the time at V = 128256).
+      const bool scan = __builtin_amdgcn_ballot_w64((unsigned)(y - row0) < (unsigned)kWaveRows) != 0;
+      float m = kNegInf, s = 0.0f, lab = 0.0f, found = 0.0f;
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          column<false>(p, acc, nb, m0, n0, tv, wm, wn, lane, xchg);
-          __builtin_amdgcn_sched_barrier(0);
+      for (int mb = 0; mb < MB; ++mb) {
+        float z[16];
+        float bm = kNegInf;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float v = acc[mb][nb][r];
+          if constexpr (CAP) v = softcap_apply(v, p.softcap, p.inv_softcap);
+          z[r] = v;
         }
-      }
-    } else {
-  #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int tc = acc_col(wn, nb, lane);
-        const int t = n0 + tc;
-        const int y_in = p.yc[t];  // t < Tvp: always inside the buffer
-        const int y = t < tv ? y_in : -1;
-        float zc[64];
-        float mx = kNegInf, lab = 0.0f, found = 0.0f;
-  #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-  #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float z = acc[mb][nb][r];
-            if constexpr (CAP) z = softcap_apply(z, p.softcap, p.inv_softcap);
-            zc[mb * 16 + r] = z;
-          }
-        // Rows past the usable vocabulary take no part: -inf drops them from
-        // both the max and the sum.  Only the tile that straddles Vu has any.
         if (ragged) {
-  #pragma unroll
-          for (int mb = 0; mb < 4; ++mb)
-  #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int v = m0 + acc_row(wm, mb, r, lane);
-              zc[mb * 16 + r] = v < p.vocab_limit ? zc[mb * 16 + r] : kNegInf;
-            }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = row0 + 32 * mb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            z[r] = (row >= m0 && row < p.vocab_limit) ? z[r] : kNegInf;
+          }
         }
-  #pragma unroll
-        for (int i = 0; i < 64; ++i) mx = __builtin_fmaxf(mx, zc[i]);
-        // The label's logit: looked for only when some lane's label falls in
-        // this wave's 128 rows (about 5% of the time at V = 128256).
-        const bool in_rows = (unsigned)(y - row0) < 128u;
-        if (__builtin_amdgcn_ballot_w64(in_rows) != 0) {
-  #pragma unroll
-          for (int mb = 0; mb < 4; ++mb)
-  #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int v = m0 + acc_row(wm, mb, r, lane);
-              lab = v == y ? zc[mb * 16 + r] : lab;
-              found = v == y ? 1.0f : found;
-            }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) bm = __builtin_fmaxf(bm, z[r]);
+        if (scan) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = row0 + 32 * mb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            const bool hit = row == y && row >= m0;
+            lab = hit ? z[r] : lab;
+            found = hit ? 1.0f : found;
+          }
         }
-        mx = __builtin_fmaxf(mx, lane_xor32(mx));
-        float s = 0.0f;
-        if (mx != kNegInf) {
-          // exp(z - mx) as one fma and the hardware base-2 exponential.
-          const float mx2 = mx * kLog2e;
-  #pragma unroll
-          for (int i = 0; i < 64; ++i) s += __builtin_amdgcn_exp2f(__builtin_fmaf(zc[i], kLog2e, -mx2));
+        const float mn = __builtin_fmaxf(m, bm);
+        if (mn != kNegInf) {
+          // exp(z - mn) as one fma and the hardware base-2 exponential; the
+          // running sum is rescaled from the old max (exp2(-inf) = 0 first).
+          const float mn2 = mn * kLog2e;
+          float bs = 0.0f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) bs += __builtin_amdgcn_exp2f(__builtin_fmaf(z[r], kLog2e, -mn2));
+          s = s * __builtin_amdgcn_exp2f(__builtin_fmaf(m, kLog2e, -mn2)) + bs;
+          m = mn;
         }
-        s += lane_xor32(s);
-        const float lab2 = lane_xor32(lab);
-        const float found2 = lane_xor32(found);
-        if (found2 != 0.0f) { lab = lab2; found = 1.0f; }
-        if (lane < 32) {
-          float* e = xchg + ((wm * 256 + tc) << 2);
-          e[0] = mx; e[1] = s; e[2] = lab; e[3] = found;
-        }
-        __builtin_amdgcn_sched_barrier(0);
       }
+      // The two lane halves hold the same token column.
+      lse_merge(m, s, lane_xor32(m), lane_xor32(s));
+      const float lab2 = lane_xor32(lab);
+      const float found2 = lane_xor32(found);
+      if (found2 != 0.0f) { lab = lab2; found = 1.0f; }
+      if (lane < 32) {
+        float* e = xchg + ((wm * 256 + tc) << 2);
+        e[0] = m; e[1] = s; e[2] = lab; e[3] = found;
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
     // Waves of the top row merge the bottom row's pairs and write out.
     if (wm == 0 && lane < 32) {
-      const int tile_v = m0 / gemm::BM;
+      const int tile_v = m0 / kTileRows;
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
         const int tc = acc_col(wn, nb, lane);

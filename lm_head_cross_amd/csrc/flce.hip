@@ -20,6 +20,7 @@
 
 #include "../../include/flce.h"
 #include "epilogues.hpp"
+#include "gemm_wide.hpp"
 #include "host_common.hpp"
 
 namespace flce {
@@ -534,26 +535,39 @@ int flce_forward(const flce_problem_t* problem, const void* hidden, const void* 
 
   const bf16* Wb = staged_head(pl, p, weight, workspace, stream);
   launch_compact_gather(pl, p, labels, hidden, meta, valid_idx, yc, device_status, lse, token_loss, xc, stream);
+  // The projection runs with 384-row head tiles (gemm_wide.hpp) when the
+  // usable head has at least that many rows, else with 256-row tiles.
+  const bool wide = pl.Vu >= gemm::WBM;
+  const int64_t tiles_v = wide ? ceil_div(pl.Vu, gemm::WBM) : pl.tiles_v;
   {
     gemm::Operand A{Wb, pl.Hp, (int)pl.Vu - 1, 0};
     gemm::Operand B{xc, pl.Hp, (int)pl.Tvp - 1, 0};
-    gemm::Schedule sch{(int)pl.tiles_v, (int)pl.tiles_t, k_steps_for(pl.Hp), tv, 2};
-    const dim3 grid(pl.tiles_v * pl.tiles_t);
+    gemm::Schedule sch{(int)tiles_v, (int)pl.tiles_t, k_steps_for(pl.Hp), tv, 2};
+    const dim3 grid(tiles_v * pl.tiles_t);
+    const float c = p.softcap, inv_c = c > 0.0f ? 1.0f / c : 0.0f;
     TraceScope tr(FLCE_KERNEL_PROJ_LSE, 2.0 * pl.T * pl.Vu * pl.H, stream);
-    if (p.softcap > 0.0f) {
-      epi::Lse<true>::Params ep{part, (int)pl.Tvp, label_logit, yc, tv, (int)pl.Vu, p.softcap, 1.0f / p.softcap};
-      hipLaunchKernelGGL((gemm::gemm_kernel<true, true, epi::Lse<true>>), grid, dim3(gemm::NTHREADS), 0, stream,
-                         A, B, sch, ep);
+    if (wide && c > 0.0f) {
+      using E = epi::Lse<true, gemm::WMB>;
+      E::Params ep{part, (int)pl.Tvp, label_logit, yc, tv, (int)pl.Vu, c, inv_c};
+      hipLaunchKernelGGL((gemm::gemm_wide_kernel<E>), grid, dim3(gemm::NTHREADS), 0, stream, A, B, sch, ep);
+    } else if (wide) {
+      using E = epi::Lse<false, gemm::WMB>;
+      E::Params ep{part, (int)pl.Tvp, label_logit, yc, tv, (int)pl.Vu, c, inv_c};
+      hipLaunchKernelGGL((gemm::gemm_wide_kernel<E>), grid, dim3(gemm::NTHREADS), 0, stream, A, B, sch, ep);
+    } else if (c > 0.0f) {
+      using E = epi::Lse<true>;
+      E::Params ep{part, (int)pl.Tvp, label_logit, yc, tv, (int)pl.Vu, c, inv_c};
+      hipLaunchKernelGGL((gemm::gemm_kernel<true, true, E>), grid, dim3(gemm::NTHREADS), 0, stream, A, B, sch, ep);
     } else {
-      epi::Lse<false>::Params ep{part, (int)pl.Tvp, label_logit, yc, tv, (int)pl.Vu, 0.0f, 0.0f};
-      hipLaunchKernelGGL((gemm::gemm_kernel<true, true, epi::Lse<false>>), grid, dim3(gemm::NTHREADS), 0, stream,
-                         A, B, sch, ep);
+      using E = epi::Lse<false>;
+      E::Params ep{part, (int)pl.Tvp, label_logit, yc, tv, (int)pl.Vu, c, inv_c};
+      hipLaunchKernelGGL((gemm::gemm_kernel<true, true, E>), grid, dim3(gemm::NTHREADS), 0, stream, A, B, sch, ep);
     }
   }
   {
     TraceScope tr(FLCE_KERNEL_COMBINE, 0.0, stream);
     hipLaunchKernelGGL(k_combine, dim3(pl.Tvp / kCombineTokens), dim3(kCombineTokens * kCombineSlices), 0, stream,
-                       (const float2*)part, (int)pl.tiles_v,
+                       (const float2*)part, (int)tiles_v,
                        (int)pl.Tvp, (const float*)label_logit, (const int32_t*)valid_idx, (const Meta*)meta, lse,
                        token_loss, bsum);
   }

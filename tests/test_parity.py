@@ -44,6 +44,12 @@ SMALL = {
     "hidden_328_fp32_head": _small(107, T=300, H=328, V=1100, Vu=1100, w_std=0.1, head_fp32=True,
                                    softcap=30.0, ignore_frac=0.05),
     "hidden_8": _small(108, T=70, H=8, V=300, Vu=290, w_std=1.0, reduction="mean", ignore_frac=0.1),
+    # the projection's 384-row head tiles: exactly one tile; two with the
+    # second shifted down over all but 16 rows of the first; one row short of
+    # a tile (256-row tiles)
+    "vocab_384": _small(109, T=260, H=128, V=384, Vu=384, w_std=0.2, softcap=15.0, ignore_frac=0.05),
+    "vocab_400": _small(110, T=300, H=256, V=420, Vu=400, w_std=0.2, ignore_frac=0.05),
+    "vocab_383": _small(111, T=200, H=128, V=383, Vu=383, w_std=0.2, ignore_frac=0.05),
 }
 
 
