@@ -8,8 +8,9 @@ path) over one batch of synthetic inputs already resident in HBM.  Prints
 one JSON line: tokens/s, the % of the bf16 dense MFMA peak that the credited
 work (8 Tv Vu H flops: projection, recompute, dX and dW) reaches, a roofline
 entry for the dominant kernel from HIP events recorded around each of its
-launches inside the timed region, and the CPU oracle timed on a bounded slice
-of the same workload.
+launches (in a second pass of as many steps, so that the events do not
+enter the timed steps), and the CPU oracle timed on a bounded slice of the
+same workload.  --graph also times one step captured as a HIP graph.
 
     python bench.py --path chunked_ce [--ce-workload ce2]
 
@@ -99,6 +100,9 @@ def main():
                     help="flce: fused linear cross-entropy (the default workload); chunked_ce: cross-entropy "
                          "over given logits")
     ap.add_argument("--ce-workload", default="ce2", help="logits-input workload for --path chunked_ce")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time one step captured as a HIP graph and replayed (an extra field; value stays "
+                         "the eager rate)")
     ap.add_argument("--fp32-head-direct", action="store_true",
                     help="hand an fp32 head to the calls as fp32 (each call rounds and stages it, inside the "
                          "timed region) instead of rounding it once before timing")
@@ -145,24 +149,33 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    trace = L.LaunchTrace(capacity=max(64, 64 * args.steps)).start()
-    # Events at each step's start, between its forward and backward, and at
-    # its end (the library launches on torch's current stream).
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # The timed steps: only the library's launches, bracketed by two events
+    # on torch's current stream (the stream the library launches on).
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # The same number of steps again with the library's launch trace (an
+    # event pair around every kernel) and events at each step's start,
+    # between its forward and backward, and at its end: the per-kernel times
+    # of the roofline and the forward / backward split.
+    trace = L.LaunchTrace(capacity=max(64, 64 * args.steps)).start()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
     for i in range(args.steps):
         ev[i][0].record()
         L.flce_forward(p, X, W, y, loss, lse, workspace=ws)
         ev[i][1].record()
         L.flce_backward(p, X, W, y, lse, g, dX, dW, workspace=ws)
         ev[i][2].record()
-    e1.record()
     torch.cuda.synchronize()
     trace.stop()
-    ms = e0.elapsed_time(e1) / args.steps
     step_ms = sorted(a.elapsed_time(c) for a, _, c in ev)
     fwd_ms = sorted(a.elapsed_time(b) for a, b, _ in ev)
     bwd_ms = sorted(b.elapsed_time(c) for _, b, c in ev)
@@ -211,6 +224,24 @@ def main():
     log(f"  per step: median {med(step_ms):.3f} ms, min {step_ms[0]:.3f} ms; forward {med(fwd_ms):.3f} ms, "
         f"backward {med(bwd_ms):.3f} ms (medians); {n_cu} CUs -> peak {peak_dev:.1f} TFLOP/s")
 
+    graph_ms = None
+    if args.graph:
+        # One step captured as a HIP graph and replayed: the same kernels
+        # without per-launch host work (reported beside the eager time).
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            step()
+        for _ in range(args.warmup):
+            gr.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            gr.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        graph_ms = e0.elapsed_time(e1) / args.steps
+        log(f"  graph replay: {graph_ms:.3f} ms per step")
+
     if args.calibration_copy_mib > 0:
         n = args.calibration_copy_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -258,6 +289,8 @@ def main():
         "kernel_source_hash": kernel_source_hash(),
         "cpu_baseline": cpu,
     }
+    if graph_ms is not None:
+        line["graph_replay_ms_per_step"] = round(graph_ms, 4)
     print(json.dumps(line), flush=True)
 
 
