@@ -8,9 +8,11 @@ path) over one batch of synthetic inputs already resident in HBM.  Prints
 one JSON line: tokens/s, the % of the bf16 dense MFMA peak that the credited
 work (8 Tv Vu H flops: projection, recompute, dX and dW) reaches, a roofline
 entry for the dominant kernel from HIP events recorded around each of its
-launches (in a second pass of as many steps, so that the events do not
-enter the timed steps), and the CPU oracle timed on a bounded slice of the
-same workload.  --graph also times one step captured as a HIP graph.
+launches inside the timed region (the trace records only that kernel's
+launches there; the per-kernel breakdown comes from the last warmup steps),
+and the CPU oracle timed on a bounded slice of the same workload.  The same
+steps without any trace are timed afterwards and reported beside it;
+--graph also times one step captured as a HIP graph.
 
     python bench.py --path chunked_ce [--ce-workload ce2]
 
@@ -145,56 +147,82 @@ def main():
         L.flce_forward(p, X, W, y, loss, lse, workspace=ws)
         L.flce_backward(p, X, W, y, lse, g, dX, dW, workspace=ws)
 
-    for _ in range(args.warmup):
+    # Warmup: the last (up to) three warmup steps run with the library's
+    # launch trace on for every kind, for the per-kernel breakdown (logged)
+    # and the dominant kernel kind.
+    n_prof = min(args.warmup, 3)
+    for _ in range(args.warmup - n_prof):
         step()
     torch.cuda.synchronize()
+    full = L.LaunchTrace(capacity=max(64, 64 * n_prof)).start()
+    for _ in range(n_prof):
+        step()
+    torch.cuda.synchronize()
+    full.stop()
 
-    # The timed steps: only the library's launches, bracketed by two events
-    # on torch's current stream (the stream the library launches on).
+    # The library prices a contraction launch at 2*T*rows*H; only the Tv
+    # valid tokens are work the method does, so rescale to 2*Tv*rows*H.
+    def by_kind(records):
+        kinds = {}
+        for kind, kms, fl in records:
+            k = kinds.setdefault(kind, {"launches": 0, "ms": 0.0, "flops": 0.0})
+            k["launches"] += 1
+            k["ms"] += kms
+            k["flops"] += fl * Tv / T
+        return kinds
+
+    def show(kinds, n_steps):
+        for name, k in sorted(kinds.items(), key=lambda kv: -kv[1]["ms"]):
+            tf = k["flops"] / (k["ms"] * 1e-3) / 1e12 if k["flops"] else 0.0
+            log(f"  {name:12s} launches={k['launches']:5d} total={k['ms'] / n_steps:8.3f} ms/step "
+                f"avg={k['ms'] / k['launches'] * 1e3:9.1f} us" + (f"  {tf:7.1f} TFLOP/s (algorithmic)" if tf else ""))
+
+    dom_name = None
+    if n_prof:
+        kinds = by_kind(full.records())
+        show(kinds, n_prof)
+        dom_name = max(kinds.items(), key=lambda kv: kv[1]["ms"])[0]
+
+    # The timed region: the launch trace records the dominant kind's launches
+    # (an event pair around each, on its stream), and events mark each step's
+    # start, the boundary between its forward and backward, and its end, all
+    # on torch's current stream, which is the stream the library launches on.
+    trace = L.LaunchTrace(capacity=max(64, 64 * args.steps), kinds=[dom_name] if dom_name else None).start()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-
-    # The same number of steps again with the library's launch trace (an
-    # event pair around every kernel) and events at each step's start,
-    # between its forward and backward, and at its end: the per-kernel times
-    # of the roofline and the forward / backward split.
-    trace = L.LaunchTrace(capacity=max(64, 64 * args.steps)).start()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
     for i in range(args.steps):
         ev[i][0].record()
         L.flce_forward(p, X, W, y, loss, lse, workspace=ws)
         ev[i][1].record()
         L.flce_backward(p, X, W, y, lse, g, dX, dW, workspace=ws)
         ev[i][2].record()
+    e1.record()
     torch.cuda.synchronize()
     trace.stop()
+    ms = e0.elapsed_time(e1) / args.steps
     step_ms = sorted(a.elapsed_time(c) for a, _, c in ev)
     fwd_ms = sorted(a.elapsed_time(b) for a, b, _ in ev)
     bwd_ms = sorted(b.elapsed_time(c) for _, b, c in ev)
     med = lambda v: v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2])
-    records = trace.records()
+    timed = by_kind(trace.records())
+    if dom_name is None:  # no warmup: every kind was traced in the timed steps
+        show(timed, args.steps)
+        dom_name = max(timed.items(), key=lambda kv: kv[1]["ms"])[0]
+    dom = timed[dom_name]
 
-    # The library prices a contraction launch at 2*T*rows*H; only the Tv
-    # valid tokens are work the method does, so rescale to 2*Tv*rows*H.
-    kinds = {}
-    for kind, kms, fl in records:
-        k = kinds.setdefault(kind, {"launches": 0, "ms": 0.0, "flops": 0.0})
-        k["launches"] += 1
-        k["ms"] += kms
-        k["flops"] += fl * Tv / T
-    for name, k in sorted(kinds.items(), key=lambda kv: -kv[1]["ms"]):
-        tf = k["flops"] / (k["ms"] * 1e-3) / 1e12 if k["flops"] else 0.0
-        log(f"  {name:12s} launches={k['launches']:5d} total={k['ms'] / args.steps:8.3f} ms/step "
-            f"avg={k['ms'] / k['launches'] * 1e3:9.1f} us" + (f"  {tf:7.1f} TFLOP/s (algorithmic)" if tf else ""))
-    dom_name, dom = max(kinds.items(), key=lambda kv: kv[1]["ms"])
+    # The same number of steps again with no events at all (reported beside
+    # the timed rate).
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    untraced_ms = e0.elapsed_time(e1) / args.steps
+
     achieved = dom["flops"] / (dom["ms"] * 1e-3) / 1e12
     traffic = None
     if os.path.exists(args.traffic_json):
@@ -223,6 +251,7 @@ def main():
         f"(credited {credited / 1e12:.2f} TFLOP)  loss={loss.item():.6g}")
     log(f"  per step: median {med(step_ms):.3f} ms, min {step_ms[0]:.3f} ms; forward {med(fwd_ms):.3f} ms, "
         f"backward {med(bwd_ms):.3f} ms (medians); {n_cu} CUs -> peak {peak_dev:.1f} TFLOP/s")
+    log(f"  without the launch trace: {untraced_ms:.3f} ms per step")
 
     graph_ms = None
     if args.graph:
@@ -282,7 +311,8 @@ def main():
             "label_tokens_per_s": round(Tv / (ms * 1e-3), 1),
         },
         "step_ms": {"median": round(med(step_ms), 4), "min": round(step_ms[0], 4),
-                    "fwd_median": round(med(fwd_ms), 4), "bwd_median": round(med(bwd_ms), 4)},
+                    "fwd_median": round(med(fwd_ms), 4), "bwd_median": round(med(bwd_ms), 4),
+                    "untraced": round(untraced_ms, 4)},
         "peak_from_device": {"compute_units": n_cu, "clock_ghz": MI355X_CLOCK_GHZ,
                              "tflops": round(peak_dev, 1)},
         "roofline": roofline,

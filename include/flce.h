@@ -220,6 +220,14 @@ typedef enum flce_kernel_kind {
  */
 int flce_trace_start(int capacity);
 
+/*
+ * Record only launches of the kinds whose bit (1 << kind) is set in
+ * kind_mask; the default, and 0xFFFFFFFF, is every kind.  Applies to launches
+ * made after the call, and stays in force across flce_trace_start.  With
+ * fewer kinds recorded, fewer events sit between the launches being timed.
+ */
+int flce_trace_select(uint32_t kind_mask);
+
 /* Stop recording; the recorded launches stay readable. */
 int flce_trace_stop(void);
 

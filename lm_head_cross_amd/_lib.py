@@ -23,7 +23,7 @@ FLCE_DTYPE_BF16 = 0
 FLCE_DTYPE_FP32 = 1
 
 EXPORTED = ("flce_status_string", "flce_version", "flce_workspace_size", "flce_forward", "flce_backward",
-            "flce_round_to_bf16", "flce_trace_start", "flce_trace_stop", "flce_trace_count", "flce_trace_get",
+            "flce_round_to_bf16", "flce_trace_start", "flce_trace_select", "flce_trace_stop", "flce_trace_count", "flce_trace_get",
             "chunked_ce_workspace_size", "chunked_ce_forward", "chunked_ce_backward", "chunked_ce_mask_labels")
 
 KERNEL_KINDS = ("compact", "gather", "proj_lse", "combine", "finalize", "recompute_g", "dweight", "dhidden",
@@ -90,6 +90,8 @@ def load() -> ctypes.CDLL:
     lib.flce_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.flce_trace_start.restype = ctypes.c_int
     lib.flce_trace_start.argtypes = [ctypes.c_int]
+    lib.flce_trace_select.restype = ctypes.c_int
+    lib.flce_trace_select.argtypes = [ctypes.c_uint32]
     lib.flce_trace_stop.restype = ctypes.c_int
     lib.flce_trace_stop.argtypes = []
     lib.flce_trace_count.restype = ctypes.c_int

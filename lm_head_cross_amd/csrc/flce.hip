@@ -693,6 +693,11 @@ int flce_trace_start(int capacity) {
   return FLCE_OK;
 }
 
+int flce_trace_select(uint32_t kind_mask) {
+  g_trace.mask = kind_mask;
+  return FLCE_OK;
+}
+
 int flce_trace_stop(void) {
   g_trace.on = false;
   return FLCE_OK;

@@ -39,6 +39,7 @@ inline unsigned grid_for(int64_t n, int64_t per_block, int64_t cap) {
 // One process-wide instance, defined in flce.hip.
 struct Tracer {
   bool on = false;
+  uint32_t mask = 0xFFFFFFFFu;  // kinds recorded (bit 1 << kind)
   int cap = 0;
   int n = 0;
   std::vector<hipEvent_t> ev;
@@ -60,7 +61,7 @@ struct TraceScope {
   int slot = -1;
   hipStream_t s;
   TraceScope(int kind, double flops, hipStream_t stream) : s(stream) {
-    if (!g_trace.on || g_trace.n >= g_trace.cap) return;
+    if (!g_trace.on || g_trace.n >= g_trace.cap || !((g_trace.mask >> kind) & 1u)) return;
     slot = g_trace.n++;
     g_trace.kind[slot] = kind;
     g_trace.flops[slot] = flops;

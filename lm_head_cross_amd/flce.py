@@ -163,15 +163,27 @@ class LaunchTrace:
     launch and waits for the events.
     """
 
-    def __init__(self, capacity: int = 4096):
+    def __init__(self, capacity: int = 4096, kinds=None):
         self.capacity = capacity
+        self.kinds = kinds
 
     def start(self):
-        _raise_for(_lib.load().flce_trace_start(self.capacity), "flce_trace_start")
+        """Start recording; with ``kinds`` (kind names), only those kinds."""
+        lib = _lib.load()
+        mask = 0xFFFFFFFF
+        if self.kinds is not None:
+            mask = 0
+            for k in self.kinds:
+                mask |= 1 << _lib.KERNEL_KINDS.index(k)
+        _raise_for(lib.flce_trace_select(mask), "flce_trace_select")
+        _raise_for(lib.flce_trace_start(self.capacity), "flce_trace_start")
         return self
 
     def stop(self):
-        _lib.load().flce_trace_stop()
+        """Stop recording; the kind filter goes back to every kind."""
+        lib = _lib.load()
+        lib.flce_trace_stop()
+        lib.flce_trace_select(0xFFFFFFFF)
 
     def records(self):
         lib = _lib.load()
