@@ -144,7 +144,7 @@ struct Lse {
 // rounded to bf16 and stored token-major, G[t][v - chunk start].  Positions
 // past the valid tokens or the chunk get 0.  (chunked_ce page,
 // _ChunkedCrossEntropySum.backward: the fp32 softmax is recomputed.)
-template <bool CAP>
+template <bool CAP, int MB = 4>
 struct Grad {
   struct Params {
     bf16* G;
@@ -158,14 +158,25 @@ struct Grad {
     const float* scale;      // g / D
     float softcap, inv_softcap;
   };
+  static constexpr int kWaveRows = 32 * MB;
 
-  static __device__ __forceinline__ void apply(const Params& p, f32x16 (&acc)[4][4], int m0, int n0,
+  static __device__ __forceinline__ void apply(const Params& p, f32x16 (&acc)[MB][4], int m0, int n0,
+                                               bf16* smem) {
+    apply(p, acc, m0, m0, n0, smem);
+  }
+
+  // m0: the tile's first chunk row; a0 <= m0: the chunk row of accumulator
+  // row 0.  A tile computed shifted down (a0 < m0) ends at the chunk's last
+  // row and stores only its rows from m0 on, one value at a time; the rows
+  // below belong to the tile before.  Otherwise rows past the chunk get 0.
+  static __device__ __forceinline__ void apply(const Params& p, f32x16 (&acc)[MB][4], int m0, int a0, int n0,
                                                bf16*) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int tv = *p.tok_count;  // > 0: tiles past the valid tokens never get here
     const float scale = *p.scale;
+    const bool shifted = a0 < m0;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const int t = n0 + acc_col(wn, nb, lane);
@@ -175,14 +186,14 @@ struct Grad {
       const int y_loc = tok_ok ? p.yc[ts] - p.v0 : -1;
       bf16* grow = p.G + (int64_t)t * p.ldg;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           bf16x4 out;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 4 * q + i;
-            const int m = m0 + acc_row(wm, mb, r, lane);
+            const int m = a0 + wm * kWaveRows + 32 * mb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
             float z = acc[mb][nb][r];
             if constexpr (CAP) z = softcap_apply(z, p.softcap, p.inv_softcap);
             float d = exp_e(z - lse_t) - (m == y_loc ? 1.0f : 0.0f);
@@ -192,7 +203,14 @@ struct Grad {
             }
             out[i] = (bf16)((tok_ok && m < p.vw) ? d * scale : 0.0f);
           }
-          *reinterpret_cast<bf16x4*>(grow + m0 + acc_row(wm, mb, 4 * q, lane)) = out;
+          const int mq = a0 + wm * kWaveRows + 32 * mb + 8 * q + 4 * (lane >> 5);
+          if (!shifted) {
+            *reinterpret_cast<bf16x4*>(grow + mq) = out;
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (mq + i >= m0) grow[mq + i] = out[i];
+          }
         }
       __builtin_amdgcn_sched_barrier(0);
     }

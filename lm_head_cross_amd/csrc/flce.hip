@@ -207,6 +207,18 @@ __global__ __launch_bounds__(256) void k_zero(uint4* __restrict__ p, int64_t n) 
     p[i] = make_uint4(0, 0, 0, 0);
 }
 
+// G[t, c0:c1] = 0 for t < rows (row stride ld): the K padding of the dH
+// contraction past a chunk's last row, which a shifted last tile of the
+// recompute does not write.
+__global__ __launch_bounds__(256) void k_zero_cols(bf16* __restrict__ G, int64_t ld, int64_t rows, int c0, int c1) {
+  const int w = c1 - c0;
+  const int64_t n = rows * w;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = i / w;
+    G[t * ld + c0 + (int)(i - t * w)] = (bf16)0.0f;
+  }
+}
+
 // fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
 __global__ __launch_bounds__(256) void k_round_bf16(const float* __restrict__ src, bf16* __restrict__ dst,
                                                      int64_t n) {
@@ -316,21 +328,31 @@ int validate(const flce_problem_t* p) {
 // depend on the split, apart from its fp32 accumulator pass, which is counted
 // with the launch overhead as a fixed cost per chunk.  Among widths up to
 // ct_max this picks the one with the least estimated time (ties: the wider).
+//
+// A chunk of at least 384 rows is recomputed with 384-row tiles (its last
+// tile shifted to end at the chunk's last row); a round of those costs
+// kWideRound of a 256-row round of the same depth: 1.5 times the work at the
+// 5-6% better rate measured on full rounds of the recompute shape.
 constexpr int64_t kChunkOverheadDepth = 1536;  // per chunk, in units of one round's depth
-int64_t pick_chunk_tiles(int64_t tiles_v, int64_t tiles_t, int64_t tiles_h, int64_t H, int64_t Tvp, int64_t ct_max,
+constexpr double kWideRound = 1.42;
+int64_t pick_chunk_tiles(int64_t Vu, int64_t tiles_t, int64_t tiles_h, int64_t H, int64_t Tvp, int64_t ct_max,
                          int n_cu) {
+  const int64_t tiles_v = ceil_div(Vu, 256);
   auto cost = [&](int64_t ct) {
     const int64_t full = tiles_v / ct;
     const int64_t rem = tiles_v - full * ct;
-    auto chunk = [&](int64_t c) {
-      return ceil_div(tiles_t * c, n_cu) * H + ceil_div(c * tiles_h, n_cu) * Tvp + kChunkOverheadDepth;
+    auto chunk = [&](int64_t c, int64_t rows) {
+      const double rec = rows >= gemm::WBM
+                             ? (double)ceil_div(ceil_div(rows, gemm::WBM) * tiles_t, n_cu) * H * kWideRound
+                             : (double)ceil_div(tiles_t * c, n_cu) * H;
+      return rec + (double)(ceil_div(c * tiles_h, n_cu) * Tvp + kChunkOverheadDepth);
     };
-    return full * chunk(ct) + (rem ? chunk(rem) : 0);
+    return full * chunk(ct, ct * 256) + (rem ? chunk(rem, Vu - full * ct * 256) : 0.0);
   };
   int64_t best = ct_max;
-  int64_t best_cost = cost(ct_max);
+  double best_cost = cost(ct_max);
   for (int64_t ct = ct_max - 1; ct >= 1; --ct) {
-    const int64_t c = cost(ct);
+    const double c = cost(ct);
     if (c < best_cost) {
       best = ct;
       best_cost = c;
@@ -369,7 +391,7 @@ Plan make_plan(const flce_problem_t* p, int n_cu = 256) {
   // sized for the widest chunk, so the workspace does not depend on the
   // device.
   const int64_t ct_max = std::max<int64_t>(1, pl.Vu / 1024);
-  const int64_t ct = pick_chunk_tiles(pl.tiles_v, pl.tiles_t, pl.tiles_h, pl.Hp, pl.Tvp, ct_max, n_cu);
+  const int64_t ct = pick_chunk_tiles(pl.Vu, pl.tiles_t, pl.tiles_h, pl.Hp, pl.Tvp, ct_max, n_cu);
   pl.vc = ct * 256;
   pl.nchunks = ceil_div(pl.tiles_v, ct);
 
@@ -631,21 +653,41 @@ int flce_backward(const flce_problem_t* problem, const void* hidden, const void*
     const bf16* Wc = W + v0 * pl.Hp;
     const double chunk_flops = 2.0 * pl.T * vw * pl.H;
 
-    // 1. logits of the chunk -> G (bf16, token-major)
+    // 1. logits of the chunk -> G (bf16, token-major); 384-row tiles when
+    //    the chunk has at least 384 rows.
     {
+      const bool wide = vw >= gemm::WBM;
+      const int64_t tiles_r = wide ? ceil_div(vw, gemm::WBM) : tiles_c;
       gemm::Operand A{Wc, pl.Hp, (int)vw - 1, 0};
       gemm::Operand B{xc, pl.Hp, (int)pl.Tvp - 1, 0};
-      gemm::Schedule sch{(int)tiles_c, (int)pl.tiles_t, k_steps_for(pl.Hp), tv, 2};
-      const dim3 grid(tiles_c * pl.tiles_t);
+      gemm::Schedule sch{(int)tiles_r, (int)pl.tiles_t, k_steps_for(pl.Hp), tv, 2};
+      const dim3 grid(tiles_r * pl.tiles_t);
+      const float c = p.softcap;
+      if (wide && vw % 128 != 0) {
+        // The dH contraction reads G's columns up to the next multiple of
+        // 128 (against zero rows of W): the shifted last tile leaves them.
+        const int c1 = (int)std::min<int64_t>(align_up((size_t)vw, 128), pl.vc);
+        TraceScope tz(FLCE_KERNEL_AUX, 0.0, stream);
+        hipLaunchKernelGGL(k_zero_cols, dim3(grid_for(pl.Tvp * (c1 - vw), 256, 1024)), dim3(256), 0, stream, G,
+                           pl.vc, pl.Tvp, (int)vw, c1);
+      }
       TraceScope tr(FLCE_KERNEL_RECOMPUTE_G, chunk_flops, stream);
-      if (p.softcap > 0.0f) {
-        epi::Grad<true>::Params ep{G, pl.vc, (int)v0, (int)vw, lse, valid_idx, yc, tv, scale, p.softcap, inv_c};
-        hipLaunchKernelGGL((gemm::gemm_kernel<true, true, epi::Grad<true>>), grid, dim3(gemm::NTHREADS), 0,
-                           stream, A, B, sch, ep);
+      if (wide && c > 0.0f) {
+        using E = epi::Grad<true, gemm::WMB>;
+        E::Params ep{G, pl.vc, (int)v0, (int)vw, lse, valid_idx, yc, tv, scale, c, inv_c};
+        hipLaunchKernelGGL((gemm::gemm_wide_kernel<E>), grid, dim3(gemm::NTHREADS), 0, stream, A, B, sch, ep);
+      } else if (wide) {
+        using E = epi::Grad<false, gemm::WMB>;
+        E::Params ep{G, pl.vc, (int)v0, (int)vw, lse, valid_idx, yc, tv, scale, 0.0f, 0.0f};
+        hipLaunchKernelGGL((gemm::gemm_wide_kernel<E>), grid, dim3(gemm::NTHREADS), 0, stream, A, B, sch, ep);
+      } else if (c > 0.0f) {
+        using E = epi::Grad<true>;
+        E::Params ep{G, pl.vc, (int)v0, (int)vw, lse, valid_idx, yc, tv, scale, c, inv_c};
+        hipLaunchKernelGGL((gemm::gemm_kernel<true, true, E>), grid, dim3(gemm::NTHREADS), 0, stream, A, B, sch, ep);
       } else {
-        epi::Grad<false>::Params ep{G, pl.vc, (int)v0, (int)vw, lse, valid_idx, yc, tv, scale, 0.0f, 0.0f};
-        hipLaunchKernelGGL((gemm::gemm_kernel<true, true, epi::Grad<false>>), grid, dim3(gemm::NTHREADS), 0,
-                           stream, A, B, sch, ep);
+        using E = epi::Grad<false>;
+        E::Params ep{G, pl.vc, (int)v0, (int)vw, lse, valid_idx, yc, tv, scale, 0.0f, 0.0f};
+        hipLaunchKernelGGL((gemm::gemm_kernel<true, true, E>), grid, dim3(gemm::NTHREADS), 0, stream, A, B, sch, ep);
       }
     }
     // 2. dH_acc (+)= G W[v0 : v0 + vw]   (M = tokens, N = H, K = chunk rows) and
