@@ -1,10 +1,11 @@
-// The forward projection's GEMM with a 384 x 256 tile (both operands
-// K-major): each of the 4 waves owns 192 x 128 of the tile as 6 x 4 blocks of
-// v_mfma_f32_32x32x16_bf16.  Against the 256 x 256 tile, a k step issues 24
-// MFMAs per 10 fragment reads (16 per 8), and a stage moves 80 KB into LDS
-// per 384 x 256 x 64 multiply-adds (64 KB per 256 x 256 x 64): about a sixth
-// less LDS and L2 traffic per flop.  On the llama3-8b head shape it measured
-// 6% faster than the 256-wide loop (same box, alternating runs).
+// The GEMM of the projection and of the backward recompute (both operands
+// K-major) with a 384 x 256 tile: each of the 4 waves owns 192 x 128 of the
+// tile as 6 x 4 blocks of v_mfma_f32_32x32x16_bf16.  Against the 256 x 256
+// tile, a k step issues 24 MFMAs per 10 fragment reads (16 per 8), and a
+// stage moves 80 KB into LDS per 384 x 256 x 64 multiply-adds (64 KB per
+// 256 x 256 x 64): about a sixth less LDS and L2 traffic per flop.  On the
+// llama3-8b head shape it measured 6% faster than the 256-wide loop, and
+// 5-6% on full rounds of the recompute shape (same box, alternating runs).
 //
 // 384 fp32 accumulators per lane do not fit the AGPR file (256).  Blocks 0-3
 // of each wave's 6 rows of blocks accumulate in AGPRs and blocks 4-5 in
@@ -18,9 +19,10 @@
 // explicitly (acc_fence).
 //
 // Two LDS stages of 80 KB (A 48 KB, B 32 KB): the whole 160 KB of a CU.
-// Every tile is full: the last head tile is computed shifted down so that it
-// ends at the last usable row, and the epilogue drops the rows that belong
-// to the tile before it.  The token operand has whole 256-row tiles.
+// Every tile is full: the last head tile (of the usable rows, or of a
+// chunk) is computed shifted down so that it ends at the last row, and the
+// epilogue drops the rows that belong to the tile before it.  The token
+// operand has whole 256-row tiles.
 #pragma once
 
 #include "gemm_tile.hpp"
