@@ -252,6 +252,7 @@ struct StoreF32 {
 // last chunk rounds to bf16 and writes each compacted token's row back to its
 // original position.
 enum { kAccFirst = 1, kAccLast = 2 };
+template <int MB = 4>
 struct AccumH {
   struct Params {
     float* acc_buf;           // [Tvp][ld] fp32
@@ -262,11 +263,21 @@ struct AccumH {
     int cols;
     int mode;
   };
-  // The running sum is read back one 64-row block (per wave: 16 rows x 4
-  // column blocks) at a time, all 64 loads in flight together: the pass is
-  // bound by memory latency, since every tile of the launch (one round of
-  // tiles) reaches it at once.  It is written back with streaming stores.
-  static __device__ __forceinline__ void apply(const Params& p, f32x16 (&acc)[4][4], int m0, int n0,
+  static constexpr int kWaveRows = 32 * MB;
+
+  static __device__ __forceinline__ void apply(const Params& p, f32x16 (&acc)[MB][4], int m0, int n0,
+                                               bf16* smem) {
+    apply(p, acc, m0, m0, n0, smem);
+  }
+
+  // m0: the tile's first token row; a0 <= m0: the row of accumulator row 0
+  // (a last tile computed shifted down); rows below m0 belong to the tile
+  // before and are left alone.  The running sum is read back one 64-row
+  // block (per wave: 16 rows x 4 column blocks) at a time, all 64 loads in
+  // flight together: the pass is bound by memory latency, since every tile
+  // of the launch (one round of tiles) reaches it at once.  It is written
+  // back with streaming stores.
+  static __device__ __forceinline__ void apply(const Params& p, f32x16 (&acc)[MB][4], int m0, int a0, int n0,
                                                bf16*) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -283,7 +294,7 @@ struct AccumH {
       hc[nb] = hok[nb] ? h : 0;   // loads stay inside the row
     }
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
       // Rows t < Tvp always exist in the running sum (rows at or past the
       // valid-token count are loaded but never used).  The first chunk reads
       // nothing: with a single chunk there is no running sum at all.
@@ -291,15 +302,16 @@ struct AccumH {
       if (!first) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t row = (int64_t)(m0 + acc_row(wm, mb, r, lane)) * p.ld;
+          const int64_t row =
+              (int64_t)(a0 + wm * kWaveRows + 32 * mb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * p.ld;
 #pragma unroll
           for (int nb = 0; nb < 4; ++nb) prev[r][nb] = p.acc_buf[row + hc[nb]];
         }
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int t = m0 + acc_row(wm, mb, r, lane);
-        if (t >= tv) continue;
+        const int t = a0 + wm * kWaveRows + 32 * mb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (t >= tv || t < m0) continue;
         const int64_t orig = last ? (int64_t)p.valid_idx[t] : 0;
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {

@@ -294,6 +294,7 @@ struct Plan {
   int64_t tiles_h;      // ceil(H / 256)
   int64_t vc;           // backward vocabulary chunk width (multiple of 256)
   int64_t nchunks;
+  int n_cu;             // compute units the chunk width was chosen for
   // workspace byte offsets
   size_t off_meta, off_valid, off_yc, off_label, off_scale, off_bsum, off_xc;
   size_t off_wst;       // the staged head [Vu, Hp] bf16 (0 bytes when the caller's head is read directly)
@@ -322,17 +323,16 @@ int validate(const flce_problem_t* p) {
 }
 
 // Width, in 256-row vocabulary tiles, of the backward pass's chunks.  A chunk
-// of ct tiles launches tiles_t * ct recompute tiles (depth H) and ct * tiles_h
-// dW tiles (depth Tvp); a launch of n tiles runs in about ceil(n / CUs)
-// rounds, one tile per CU per round.  The dH contraction's cost does not
-// depend on the split, apart from its fp32 accumulator pass, which is counted
-// with the launch overhead as a fixed cost per chunk.  Among widths up to
-// ct_max this picks the one with the least estimated time (ties: the wider).
-//
-// A chunk of at least 384 rows is recomputed with 384-row tiles (its last
-// tile shifted to end at the chunk's last row); a round of those costs
-// kWideRound of a 256-row round of the same depth: 1.5 times the work at the
-// 5-6% better rate measured on full rounds of the recompute shape.
+// of ct tiles launches tiles_t * ceil(256 ct / 384) recompute tiles (depth H;
+// 256-row tiles for chunks under 384 rows) and ct * tiles_h dW tiles (depth
+// Tvp); a launch of n tiles runs in about ceil(n / CUs) rounds, one tile per
+// CU per round.  The dH contraction's cost does not depend on the split,
+// apart from its fp32 accumulator pass, which is counted with the launch
+// overhead as a fixed cost per chunk.  Among widths up to ct_max this picks
+// the one with the least estimated time (ties: the wider).  A round of
+// 384-row recompute tiles costs kWideRound 256-row rounds of the same depth:
+// 1.5 times the work at the 5-6% better rate measured on full rounds of the
+// recompute shape.
 constexpr int64_t kChunkOverheadDepth = 1536;  // per chunk, in units of one round's depth
 constexpr double kWideRound = 1.42;
 int64_t pick_chunk_tiles(int64_t Vu, int64_t tiles_t, int64_t tiles_h, int64_t H, int64_t Tvp, int64_t ct_max,
@@ -359,6 +359,20 @@ int64_t pick_chunk_tiles(int64_t Vu, int64_t tiles_t, int64_t tiles_h, int64_t H
     }
   }
   return best;
+}
+
+// Whether a chunk's dH runs on 384-row token tiles (it needs at least 384
+// token rows).  The wide tile is about 9% faster per flop, but the launch
+// hands out dH's deep tiles before dW's, and the tile counts decide how the
+// two pack onto the compute units.  Measured back to back, all chunks wide
+// against all narrow: workloads 3, 4 and 5 (384, 640 and 8032 narrow dH
+// tiles per chunk on the device) gained 2.1%, 2.9% and 5.1% per step;
+// workload 2, whose 256 narrow dH tiles fill exactly one round of the 256
+// compute units, lost 1.3%.  So the narrow tiles are kept when they make
+// exactly one full round.  (The host sees T, not the valid count.)
+bool dh_wide(int64_t tiles_t, int64_t tiles_h, int64_t Tvp, int n_cu) {
+  if (Tvp < gemm::WBM) return false;
+  return tiles_t * tiles_h != n_cu;
 }
 
 // Compute units of the current device (256 on MI355X when the query fails).
@@ -393,6 +407,7 @@ Plan make_plan(const flce_problem_t* p, int n_cu = 256) {
   const int64_t ct_max = std::max<int64_t>(1, pl.Vu / 1024);
   const int64_t ct = pick_chunk_tiles(pl.Vu, pl.tiles_t, pl.tiles_h, pl.Hp, pl.Tvp, ct_max, n_cu);
   pl.vc = ct * 256;
+  pl.n_cu = n_cu;
   pl.nchunks = ceil_div(pl.tiles_v, ct);
 
   size_t o = 0;
@@ -646,6 +661,7 @@ int flce_backward(const flce_problem_t* problem, const void* hidden, const void*
   zero_fill(d_weight + pl.Vu * pl.H, (pl.V - pl.Vu) * pl.H * 4, stream);
 
   const float inv_c = p.softcap > 0.0f ? 1.0f / p.softcap : 0.0f;
+  const bool wide_h = dh_wide(pl.tiles_t, pl.tiles_h, pl.Tvp, pl.n_cu);
   for (int64_t c = 0; c < pl.nchunks; ++c) {
     const int64_t v0 = c * pl.vc;
     const int64_t vw = std::min(pl.vc, pl.Vu - v0);
@@ -692,25 +708,35 @@ int flce_backward(const flce_problem_t* problem, const void* hidden, const void*
     }
     // 2. dH_acc (+)= G W[v0 : v0 + vw]   (M = tokens, N = H, K = chunk rows) and
     //    dW[v0 : v0 + vw] = G^T Xc          (M = chunk rows, N = H, K = tokens)
-    //    in one launch, dH's tiles first.  dH's K-major G and MN-major W;
-    //    dW reads G MN-major (transposing LDS reads) and Xc K-major from XcT.
+    //    in one launch, dH's tiles first.  dH's K-major G and MN-major W, on
+    //    384-row token tiles when there are at least 384 token rows; dW reads
+    //    G MN-major (transposing LDS reads) and Xc K-major from XcT.
     {
+      const int64_t tiles_hm = wide_h ? ceil_div(pl.Tvp, gemm::WBM) : pl.tiles_t;
       gemm::Operand Ah{G, pl.vc, (int)pl.Tvp - 1, 0};
       gemm::Operand Bh{Wc, pl.Hp, (int)pl.H - 1, (int)vw - 1};
-      gemm::Schedule sh{(int)pl.tiles_t, (int)pl.tiles_h, k_steps_for(vw), tv, 1};
+      gemm::Schedule sh{(int)tiles_hm, (int)pl.tiles_h, k_steps_for(vw), tv, 1};
       int mode = 0;
       if (c == 0) mode |= epi::kAccFirst;
       if (c == pl.nchunks - 1) mode |= epi::kAccLast;
-      epi::AccumH::Params eh{hacc, pl.H, (bf16*)d_hidden, valid_idx, tv, (int)pl.H, mode};
       gemm::Operand Aw{G, pl.vc, (int)pl.vc - 1, (int)pl.Tvp - 1};
       gemm::Operand Bw{xct, pl.Tvp, (int)pl.H - 1, 0};
       gemm::Schedule sw{(int)tiles_c, (int)pl.tiles_h, 0, tv, 3};
       epi::StoreF32::Params ew{d_weight + v0 * pl.H, pl.H, (int)vw, (int)pl.H};
-      const int64_t n_h = align_up((size_t)(pl.tiles_t * pl.tiles_h), 8);
+      const int64_t n_h = align_up((size_t)(tiles_hm * pl.tiles_h), 8);
+      const dim3 grid(n_h + tiles_c * pl.tiles_h);
       TraceScope tr(FLCE_KERNEL_DGRAD, 2.0 * chunk_flops, stream);
-      hipLaunchKernelGGL((gemm::gemm_pair<true, false, epi::AccumH, false, true, epi::StoreF32>),
-                         dim3(n_h + tiles_c * pl.tiles_h), dim3(gemm::NTHREADS), 0, stream, Ah, Bh, sh, eh, (int)n_h,
-                         Aw, Bw, sw, ew);
+      if (wide_h) {
+        using EH = epi::AccumH<gemm::WMB>;
+        EH::Params eh{hacc, pl.H, (bf16*)d_hidden, valid_idx, tv, (int)pl.H, mode};
+        hipLaunchKernelGGL((gemm::gemm_pair_wide<EH, epi::StoreF32>), grid, dim3(gemm::NTHREADS), 0, stream, Ah,
+                           Bh, sh, eh, (int)n_h, Aw, Bw, sw, ew);
+      } else {
+        using EH = epi::AccumH<>;
+        EH::Params eh{hacc, pl.H, (bf16*)d_hidden, valid_idx, tv, (int)pl.H, mode};
+        hipLaunchKernelGGL((gemm::gemm_pair<true, false, EH, false, true, epi::StoreF32>), grid,
+                           dim3(gemm::NTHREADS), 0, stream, Ah, Bh, sh, eh, (int)n_h, Aw, Bw, sw, ew);
+      }
     }
   }
   return launch_status();

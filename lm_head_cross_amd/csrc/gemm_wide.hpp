@@ -190,6 +190,149 @@ __device__ __forceinline__ void mainloop_w(const Operand& A, const Operand& B, i
   acc_fence(acc);
 }
 
+// ---- K-major A (384 rows) x MN-major B (256 columns): the dH contraction.
+// B's fragments come from transposing reads (ds_read_b64_tr_b16), the slow
+// ones, so each k step reads the next step's 4 B fragments first, after its
+// first four MFMAs.  A's fragments use one register set: the next step's
+// fragment i is read into fa[i] right after the step's last MFMA with it
+// (the MFMAs run i-major), which leaves the registers that a second set
+// would take to the 128 VGPR accumulators.
+
+// MN-major operand: a stage is 64 k-rows x 256 columns (rows of 512 bytes);
+// each wave DMAs 8 blocks of 2 k-rows.  Block b's k-row offset is uniform
+// (scalar offset); a lane's offset within its block depends only on b's
+// parity (the pair swizzle of k-row 2b + lane/32 repeats every 4 k-rows).
+// k-rows past k_max read as zero.
+struct MnLoaderW {
+  const bf16* base;
+  int64_t ld;
+  int k_max;
+  unsigned off[2];
+  __device__ __forceinline__ MnLoaderW(const Operand& op, int mn0, int lane) {
+    base = op.ptr;
+    ld = op.ld;
+    k_max = op.k_max;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int kk = q * 2 + (lane >> 5);
+      const int c = (lane & 31) ^ swz_mn(kk);
+      const int col = min(mn0 + c * 8, op.mn_max - 7);
+      off[q] = (unsigned)((lane >> 5) * (int)op.ld + col) * 2u;
+    }
+  }
+  __device__ __forceinline__ void issue(bf16* tile, int k0, int wave, int q) const {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (int64_t)k0 * ld);
+    const int b = wave * 8 + q;
+    const unsigned soff = __builtin_amdgcn_readfirstlane((unsigned)(b * 2) * (unsigned)ld * 2u);
+    if (k0 + BK2 - 1 <= k_max) {
+      lds_dma16(r, off[q & 1], soff, tile + b * 512);
+    } else {
+      const int kk = b * 2 + (int)((threadIdx.x >> 5) & 1);
+      lds_dma16(r, kk <= k_max - k0 ? off[q & 1] : 0x80000000u, soff, tile + b * 512);
+    }
+  }
+};
+
+// frag_mnmajor with the second read's index laundered by a volatile asm
+// (the alias-scope reason is given at frag_mnmajor): a non-volatile one is
+// hoisted out of the main loop, and the 16 indices it then keeps live spill
+// with this tile's register budget.
+__device__ __forceinline__ bf16x8 frag_mn_w(const bf16* tile, int col0, int s, int lane) {
+  const int g = lane >> 4;
+  const int j = lane & 15;
+  const int col = col0 + 16 * (g & 1) + 4 * (j & 3);
+  const int k0 = 16 * s + 8 * (g >> 1) + (j >> 2);
+  const int k1 = k0 + 4;
+  const int i0 = k0 * 256 + (((col >> 3) ^ swz_mn(k0)) << 3) + (col & 7);
+  int i1 = k1 * 256 + (((col >> 3) ^ swz_mn(k1)) << 3) + (col & 7);
+  asm volatile("" : "+v"(i1));
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((FLCE_LDS bf16x4*)(tile + i0));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((FLCE_LDS bf16x4*)(tile + i1));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <bool RD, int NV, class DmaF>
+__device__ __forceinline__ void kstep_kmn(f32x16 (&acc)[WMB][4], bf16x8 (&fa)[WMB], const bf16x8 (&fb)[4],
+                                          bf16x8 (&nb)[4], const bf16* sa, const bf16* sb, int s_next, int wm,
+                                          int wn, int lane, DmaF dma) {
+#pragma unroll
+  for (int m = 0; m < 4 * WMB; ++m) {
+    const int i = m / 4, j = m % 4;
+    if (i < 4) mfma_agpr(acc[i][j], fa[i], fb[j]);
+    else mfma_vgpr(acc[i][j], fa[i], fb[j]);
+    if (RD && m < 4) nb[m] = frag_mn_w(sb, wn * 128 + 32 * m, s_next, lane);
+    if (RD && j == 3) fa[i] = frag64(sa, wm * 32 * WMB + 32 * i + (lane & 31), s_next, lane);
+    if constexpr (NV > 0) {
+#pragma unroll
+      for (int d = 0; d < NV; ++d)
+        if (m == 1 + (4 * WMB * d) / NV) dma(d);
+    }
+  }
+}
+
+// Same stage order, DMA split and barrier as stage_w.
+template <bool NEXT, bool NEXT2>
+__device__ __forceinline__ void stage_kmn(bf16* ca, bf16* cb, bf16* na, bf16* nb, int D, const FullLoader<WNBA>& la,
+                                          const MnLoaderW& lb, int wave, int wm, int wn, int lane,
+                                          bf16x8 (&fa)[WMB], bf16x8 (&fb)[2][4], f32x16 (&acc)[WMB][4]) {
+  const int k1 = (D + 1) * BK2, k2 = (D + 2) * BK2;
+  auto dma0 = [&](int d) {
+    if (d < WNBA - 8) la.issue(na, k1, wave, 8 + d);
+    else lb.issue(nb, k1, wave, d - (WNBA - 8));
+  };
+  auto dma1 = [&](int d) { lb.issue(nb, k1, wave, 4 + d); };
+  auto dma3 = [&](int d) { la.issue(ca, k2, wave, d); };
+  if constexpr (NEXT) kstep_kmn<true, WNBA - 4>(acc, fa, fb[0], fb[1], ca, cb, 1, wm, wn, lane, dma0);
+  else kstep_kmn<true, 0>(acc, fa, fb[0], fb[1], ca, cb, 1, wm, wn, lane, NoDma{});
+  if constexpr (NEXT) kstep_kmn<true, 4>(acc, fa, fb[1], fb[0], ca, cb, 2, wm, wn, lane, dma1);
+  else kstep_kmn<true, 0>(acc, fa, fb[1], fb[0], ca, cb, 2, wm, wn, lane, NoDma{});
+  kstep_kmn<true, 0>(acc, fa, fb[0], fb[1], ca, cb, 3, wm, wn, lane, NoDma{});
+  if constexpr (NEXT) {
+    stage_barrier<0>();
+    if constexpr (NEXT2) kstep_kmn<true, 8>(acc, fa, fb[1], fb[0], na, nb, 0, wm, wn, lane, dma3);
+    else kstep_kmn<true, 0>(acc, fa, fb[1], fb[0], na, nb, 0, wm, wn, lane, NoDma{});
+  } else {
+    kstep_kmn<false, 0>(acc, fa, fb[1], fb[0], na, nb, 0, wm, wn, lane, NoDma{});
+  }
+}
+
+__device__ __forceinline__ void mainloop_kmn(const Operand& A, const Operand& B, int a0, int n0, int nk, bf16* s0,
+                                            bf16* s1, bf16* s2, bf16* s3, f32x16 (&acc)[WMB][4]) {
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int i = 0; i < WMB; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  acc_fence(acc);
+  const int nd = nk / 2;
+  const FullLoader<WNBA> la(A, a0, wave, lane);
+  const MnLoaderW lb(B, n0, lane);
+#pragma unroll
+  for (int q = 0; q < WNBA; ++q) la.issue(s0, 0, wave, q);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) lb.issue(s1, 0, wave, q);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) la.issue(s2, BK2, wave, q);
+  stage_barrier<8>();
+  bf16x8 fa[WMB], fb[2][4];
+#pragma unroll
+  for (int r = 0; r < WMB; ++r) fa[r] = frag64(s0, wm * 32 * WMB + 32 * r + (lane & 31), 0, lane);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) fb[0][r] = frag_mn_w(s1, wn * 128 + 32 * r, 0, lane);
+  int D = 0;
+  for (; D + 2 < nd; D += 2) {
+    stage_kmn<true, true>(s0, s1, s2, s3, D, la, lb, wave, wm, wn, lane, fa, fb, acc);
+    stage_kmn<true, true>(s2, s3, s0, s1, D + 1, la, lb, wave, wm, wn, lane, fa, fb, acc);
+  }
+  stage_kmn<true, false>(s0, s1, s2, s3, D, la, lb, wave, wm, wn, lane, fa, fb, acc);
+  stage_kmn<false, false>(s2, s3, s0, s1, D + 1, la, lb, wave, wm, wn, lane, fa, fb, acc);
+  stage_barrier<0>();
+  acc_fence(acc);
+}
+
 // Tile order as tile_of, with groups of WIDE_GROUP_M M-tiles (the 32
 // workgroups of an XCD then cover 4 x 8 tiles).
 __device__ __forceinline__ void tile_of_wide(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
@@ -232,6 +375,40 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_wide_kernel(Operand A, Opera
   f32x16 acc[WMB][4];
   mainloop_w(A, B, a0, n0, sch.k_steps, s0, s1, s2, s3, acc);
   Epi::apply(ep, acc, m0, a0, n0, s0);
+}
+
+// dH of one chunk (K-major G x MN-major W with 384-row token tiles) and dW
+// of the chunk (run_tile's MN-major G x K-major XcT, 256-row tiles) in one
+// launch.  Workgroups [0, n1) take dH's tiles (n1: its host-side tile count
+// rounded up to a multiple of 8, so that dW's tiles keep the id-to-XCD
+// mapping tile_of assumes), the rest dW's.  Only the ceil(Tv / 384) token
+// tiles that hold valid tokens run; the last is computed shifted down to
+// end at row Tvp - 1 (G's rows past Tv are zero).
+template <class Epi1, class Epi2>
+__global__ __launch_bounds__(NTHREADS, 1) void gemm_pair_wide(Operand A1, Operand B1, Schedule sch1,
+                                                               typename Epi1::Params ep1, int n1, Operand A2,
+                                                               Operand B2, Schedule sch2, typename Epi2::Params ep2) {
+  __shared__ __attribute__((aligned(1024))) bf16 s0[WSTAGE_A];
+  __shared__ __attribute__((aligned(1024))) bf16 s1[STAGE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 s2[WSTAGE_A];
+  __shared__ __attribute__((aligned(1024))) bf16 s3[STAGE_ELEMS];
+  const int pid = blockIdx.x;
+  if (pid < n1) {
+    const int tv = *sch1.tok_count;
+    const int tiles_m = min(sch1.tiles_m, (tv + WBM - 1) / WBM);
+    const int tiles_n = sch1.tiles_n;
+    if (pid >= tiles_m * tiles_n) return;
+    int tm, tn;
+    tile_of_wide(pid, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * WBM;
+    const int a0 = min(m0, A1.mn_max + 1 - WBM);
+    const int n0 = tn * BN;
+    f32x16 acc[WMB][4];
+    mainloop_kmn(A1, B1, a0, n0, sch1.k_steps, s0, s1, s2, s3, acc);
+    Epi1::apply(ep1, acc, m0, a0, n0, s0);
+  } else {
+    run_tile<false, true, Epi2>(A2, B2, sch2, ep2, pid - n1, s0, s1, s2, s3);
+  }
 }
 
 }  // namespace gemm
