@@ -1,11 +1,13 @@
-// The GEMM of the projection and of the backward recompute (both operands
-// K-major) with a 384 x 256 tile: each of the 4 waves owns 192 x 128 of the
-// tile as 6 x 4 blocks of v_mfma_f32_32x32x16_bf16.  Against the 256 x 256
-// tile, a k step issues 24 MFMAs per 10 fragment reads (16 per 8), and a
-// stage moves 80 KB into LDS per 384 x 256 x 64 multiply-adds (64 KB per
-// 256 x 256 x 64): about a sixth less LDS and L2 traffic per flop.  On the
-// llama3-8b head shape it measured 6% faster than the 256-wide loop, and
-// 5-6% on full rounds of the recompute shape (same box, alternating runs).
+// GEMMs with a 384 x 256 tile: the projection and the backward recompute
+// (both operands K-major, mainloop_w), and dH (K-major G x MN-major W,
+// mainloop_kmn).  Each of the 4 waves owns 192 x 128 of the tile as 6 x 4
+// blocks of v_mfma_f32_32x32x16_bf16.  Against the 256 x 256 tile, a k step
+// issues 24 MFMAs per 10 fragments (16 per 8), and a stage moves 80 KB into
+// LDS per 384 x 256 x 64 multiply-adds (64 KB per 256 x 256 x 64): about a
+// sixth less LDS and L2 traffic per flop.  Measured against the 256-wide
+// loops (same box, alternating runs): 6% faster on the llama3-8b head's
+// projection, 5-6% on full rounds of the recompute shape, 10.8% on full
+// rounds of the dH shape.
 //
 // 384 fp32 accumulators per lane do not fit the AGPR file (256).  Blocks 0-3
 // of each wave's 6 rows of blocks accumulate in AGPRs and blocks 4-5 in
