@@ -1,4 +1,5 @@
-"""The fused path under HIP graph capture (torch.cuda.CUDAGraph).
+"""The fused path under HIP graph capture (torch.cuda.CUDAGraph), and the
+launch trace's kind filter.
 
 The library allocates nothing, sets no memory with memset nodes and never
 synchronises the host, so a forward + backward pass can be captured once and
@@ -88,3 +89,27 @@ def test_captured_step_replays_match_eager(name):
     got = _snapshot(o)
     for k in ("loss", "lse", "tl", "dX", "dW"):
         assert torch.equal(got[k], eager2[k]), ("new input", k)
+
+
+def test_launch_trace_kind_filter():
+    """The launch trace records only the selected kinds, and after stop()
+    every kind again (the bench times its dominant kernel this way)."""
+    d = torch.device("cuda:0")
+    inp = make_inputs(SMALL["multichunk_sum_runs"])
+    p, X, W, y, o = _buffers(inp, d)
+    _step(p, X, W, y, o)
+    torch.cuda.synchronize()
+    tr = L.LaunchTrace(capacity=256, kinds=["dgrad"]).start()
+    _step(p, X, W, y, o)
+    torch.cuda.synchronize()
+    tr.stop()
+    rec = tr.records()
+    assert rec and all(k == "dgrad" for k, _, _ in rec)
+    assert all(ms > 0 and fl > 0 for _, ms, fl in rec)
+    full = L.LaunchTrace(capacity=256).start()
+    _step(p, X, W, y, o)
+    torch.cuda.synchronize()
+    full.stop()
+    kinds = {k for k, _, _ in full.records()}
+    assert {"proj_lse", "recompute_g", "dgrad", "compact", "gather"} <= kinds
+    assert sum(k == "dgrad" for k, _, _ in full.records()) == len(rec)
