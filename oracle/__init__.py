@@ -6,5 +6,5 @@ leg may import this package; the product path never does.
 """
 from .flce_oracle import *  # noqa: F401,F403
 from .flce_oracle import Forward, Problem  # noqa: F401
-from .chunked_ce_oracle import (CEProblem, apply_mask, ce_backward, ce_forward, ce_lse, ce_rows,  # noqa: F401
-                                check_ce_problem)
+from .chunked_ce_oracle import (CEProblem, apply_mask, ce_backward, ce_forward, ce_label_logits,  # noqa: F401
+                                ce_loss_from_lse, ce_lse, ce_rows, check_ce_problem)

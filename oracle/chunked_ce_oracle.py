@@ -46,7 +46,8 @@ import math
 
 import numpy as np
 
-from .flce_oracle import REDUCTIONS, Forward, Problem, divisor, logit_grad, logsumexp_rows, valid_positions
+from .flce_oracle import (REDUCTIONS, Forward, Problem, divisor, logit_grad, logsumexp_rows, loss_from_lse,
+                          valid_positions)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -136,3 +137,19 @@ def ce_rows(logits_rows, lab_rows, lse_rows, scale: float) -> np.ndarray:
 def ce_lse(logits_rows) -> np.ndarray:
     """lse of the given rows (label independent)."""
     return logsumexp_rows(np.asarray(logits_rows, dtype=np.float64))
+
+
+def ce_label_logits(logits_rows, lab_rows) -> np.ndarray:
+    """z[i, y_i] for the given (valid) rows: the label's own logit."""
+    z = np.asarray(logits_rows, dtype=np.float64)
+    lab = np.asarray(lab_rows, dtype=np.int64)
+    return z[np.arange(z.shape[0]), lab]
+
+
+def ce_loss_from_lse(lse, label_logit, labels, p: CEProblem, vocab: int) -> Forward:
+    """Per-position loss, exact total and loss from each counted position's
+    lse and label logit ([T] arrays, values at ignored positions unread).
+    ``labels`` are the labels after the mask was applied (:func:`apply_mask`)."""
+    lab = np.asarray(labels, dtype=np.int64).reshape(-1)
+    check_ce_problem(p, vocab, lab)
+    return loss_from_lse(lse, label_logit, lab, _as_linear_problem(p, vocab))

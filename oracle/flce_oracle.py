@@ -54,8 +54,9 @@ import numpy as np
 def round_fp32_to_bf16(a) -> np.ndarray:
     """Round float32 values to the nearest bfloat16, ties to even.
 
-    The Inkling2 loss page (class description) rounds an fp32 head to bf16
-    with the cast FSDP applies; torch's fp32->bf16 cast rounds to nearest even.
+    The Inkling2 loss page (class description) uses an fp32 head at its bf16
+    value, the rounding sharded training applies; torch's fp32->bf16 cast
+    rounds to nearest even.
     Works on the IEEE bit patterns: keep the high 16 bits after adding
     0x7FFF plus the lowest kept bit.  NaN stays NaN (quiet).  Returns the
     rounded values as float64 (exactly representable).
@@ -286,6 +287,30 @@ def label_logits(X, W, labels, p: Problem) -> np.ndarray:
     z = np.einsum("th,th->t", X[idx], np.asarray(W, dtype=np.float64)[labels[idx]])
     out[idx] = softcap(z, p.softcap)
     return out
+
+
+def loss_from_lse(lse, label_logit, labels, p: Problem) -> Forward:
+    """The definition's last steps from each token's lse and label logit.
+
+    For every valid position the token loss is lse_t - z'[t, y_t] (0 where
+    the label is ``ignore_index``); the total S is their exact sum, and the
+    loss is S / D with the normaliser of the reduction.  ``lse`` and
+    ``label_logit`` are [T] arrays whose values at ignored positions are not
+    read (the large workloads take them from :func:`token_lse` and
+    :func:`label_logits`).
+    """
+    labels = np.asarray(labels, dtype=np.int64)
+    valid = valid_positions(labels, p.ignore_index)
+    lse = np.asarray(lse, dtype=np.float64)
+    ll = np.asarray(label_logit, dtype=np.float64)
+    tl = np.zeros(labels.shape[0])
+    tl[valid] = lse[valid] - ll[valid]
+    lse_out = np.where(valid, lse, np.nan)
+    S = math.fsum(tl.tolist())
+    n = int(valid.sum())
+    D = divisor(p, n)
+    loss = S / D if D != 0 else float("nan")
+    return Forward(loss, tl, lse_out, n, D, S)
 
 
 def token_rows(X, W, labels, rows, p: Problem, D: float, grad_out: float = 1.0):

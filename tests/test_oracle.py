@@ -363,3 +363,41 @@ def test_sampled_evaluation_matches_dense(c, reduction, nlt):
     vrows = np.array([0, 1, 255, 256, 400, 511])
     dWr = oracle.weight_rows(X, W, y, vrows, lse_all, p, fw.D, grad_out=0.5, token_block=77)
     np.testing.assert_allclose(dWr, dW[vrows], rtol=1e-10, atol=1e-14)
+
+
+@pytest.mark.parametrize("c,reduction,nlt,Vu", [(0.0, "sum", None, 530), (30.0, "mean", None, 512),
+                                                (2.0, "sum", 77, 500), (0.0, "mean", 1234, 530)])
+def test_loss_from_lse_matches_torch_cross_entropy(c, reduction, nlt, Vu):
+    """The sampled path of the large workloads (lse of every token, one label
+    logit per token, then loss_from_lse) gives PyTorch's fp64 cross entropy:
+    the per-token losses, the sum S, the divisor D and the loss."""
+    rng = np.random.default_rng(31)
+    T, H, V = 200, 40, 530
+    X = rng.standard_normal((T, H))
+    W = rng.standard_normal((V, H)) / math.sqrt(H) * 3
+    y = _labels(rng, T, Vu, 23)
+    p = Problem(Vu, c, -100, reduction, nlt)
+    lse = oracle.token_lse(X, W, p, row_block=64)
+    ll = oracle.label_logits(X, W, y, p)
+    got = oracle.loss_from_lse(lse, ll, y, p)
+    z = torch.tensor(X) @ torch.tensor(W[:Vu]).T
+    if c > 0:
+        z = c * torch.tanh(z / c)
+    yt = torch.tensor(y)
+    ref_tok = F.cross_entropy(z, yt, ignore_index=-100, reduction="none").numpy()
+    np.testing.assert_allclose(got.token_loss, ref_tok, rtol=1e-12, atol=1e-12)
+    if nlt is None:
+        ref = F.cross_entropy(z, yt, ignore_index=-100, reduction=reduction).item()
+    else:
+        ref = F.cross_entropy(z, yt, ignore_index=-100, reduction="sum").item() / nlt
+    assert got.loss == pytest.approx(ref, rel=1e-12)
+    assert got.n_valid == int((y != -100).sum())
+    assert got.S == pytest.approx(float(ref_tok.sum()), rel=1e-12)
+    assert got.D == (nlt if nlt is not None else (got.n_valid if reduction == "mean" else 1.0))
+    assert np.all(np.isnan(got.lse[y == -100]))
+    # values at ignored positions are never read
+    lse2 = lse.copy()
+    ll2 = ll.copy()
+    lse2[y == -100] = np.inf
+    ll2[y == -100] = np.nan
+    assert oracle.loss_from_lse(lse2, ll2, y, p).loss == got.loss

@@ -169,3 +169,70 @@ def test_no_valid_position():
     assert ce_forward(z, y, CEProblem()).loss == 0.0
     assert math.isnan(ce_forward(z, y, CEProblem(reduction="mean")).loss)
     assert np.all(ce_backward(z, y, CEProblem(reduction="mean")) == 0)
+
+
+@pytest.mark.parametrize("reduction,nlt,g", [("sum", None, 1.0), ("mean", None, -0.75), ("sum", 40, 2.5)])
+def test_row_helpers_match_whole_problem(reduction, nlt, g):
+    """ce_lse, ce_label_logits, ce_rows and ce_loss_from_lse (the sampled path
+    of the full-size logits workloads) give, row by row, what ce_forward and
+    ce_backward give for the whole problem, and PyTorch's fp64 cross entropy.
+    Logit scales differ by row, so swapping ce_rows' lse and label arguments,
+    or taking another row's lse, fails."""
+    rng = np.random.default_rng(13)
+    T, V = 40, 97
+    z = rng.normal(0.0, 1.0, (T, V)) * rng.uniform(0.5, 6.0, (T, 1)) + rng.normal(0.0, 5.0, (T, 1))
+    y = rng.integers(0, V, T)
+    y[[3, 11, 30]] = -100
+    p = CEProblem(reduction=reduction, num_label_tokens=nlt)
+    fw = ce_forward(z, y, p)
+    dz = ce_backward(z, y, p, grad_out=g)
+    idx = np.nonzero(y != -100)[0]
+    lse_rows = oracle.ce_lse(z[idx])
+    np.testing.assert_allclose(lse_rows, fw.lse[idx], rtol=1e-14)
+    np.testing.assert_allclose(lse_rows, torch.logsumexp(torch.tensor(z[idx]), dim=1).numpy(), rtol=1e-13)
+    ll = oracle.ce_label_logits(z[idx], y[idx])
+    assert np.array_equal(ll, z[idx, y[idx]])
+    lse_all = np.full(T, np.nan)
+    lse_all[idx] = lse_rows
+    ll_all = np.zeros(T)
+    ll_all[idx] = ll
+    got = oracle.ce_loss_from_lse(lse_all, ll_all, y, p, V)
+    np.testing.assert_allclose(got.token_loss, fw.token_loss, rtol=1e-13, atol=1e-14)
+    assert got.loss == pytest.approx(fw.loss, rel=1e-13)
+    assert (got.S, got.D, got.n_valid) == pytest.approx((fw.S, fw.D, fw.n_valid), rel=1e-13)
+    zt = torch.tensor(z, requires_grad=True)
+    red = "sum" if nlt is not None else reduction
+    ref = F.cross_entropy(zt, torch.tensor(y), ignore_index=-100, reduction=red)
+    if nlt is not None:
+        ref = ref / nlt
+    (ref * g).backward()
+    assert got.loss == pytest.approx(ref.item(), rel=1e-12)
+    rows = oracle.ce_rows(z[idx], y[idx], lse_rows, g / fw.D)
+    np.testing.assert_allclose(rows, dz[idx], rtol=1e-13, atol=1e-16)
+    np.testing.assert_allclose(rows, zt.grad.numpy()[idx], rtol=1e-11, atol=1e-15)
+
+
+def test_negative_infinite_logits():
+    """Columns at -inf (masked vocabulary entries) add nothing to the softmax:
+    the loss and the other columns' gradient equal those of the problem
+    without the columns, PyTorch agrees, and the gradient there is 0."""
+    rng = np.random.default_rng(17)
+    T, V = 12, 40
+    z = rng.normal(0.0, 3.0, (T, V))
+    dead = np.array([0, 1, 2, 9, 20, 21, 39])
+    z[:, dead] = -np.inf
+    keep = np.setdiff1d(np.arange(V), dead)
+    y = keep[rng.integers(0, len(keep), T)]
+    y[4] = -100
+    p = CEProblem(reduction="mean")
+    fw = ce_forward(z, y, p)
+    dz = ce_backward(z, y, p)
+    remap = np.full(V, -1)
+    remap[keep] = np.arange(len(keep))
+    y_k = np.where(y == -100, -100, remap[np.maximum(y, 0)])
+    ref = ce_forward(z[:, keep], y_k, p)
+    assert np.isfinite(fw.loss) and fw.loss == pytest.approx(ref.loss, rel=1e-14)
+    np.testing.assert_allclose(dz[:, keep], ce_backward(z[:, keep], y_k, p), rtol=1e-14, atol=1e-17)
+    assert np.all(dz[:, dead] == 0.0)
+    zt = torch.tensor(z)
+    assert fw.loss == pytest.approx(F.cross_entropy(zt, torch.tensor(y), ignore_index=-100).item(), rel=1e-13)
