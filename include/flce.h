@@ -19,9 +19,9 @@
  * Sources (NVIDIA NeMo AutoModel API pages):
  *  - "nemo_automodel.components.models.inkling2.loss",
  *    Inkling2FusedLinearCrossEntropy (constructor and class description):
- *    bf16 x bf16 projection with fp32 accumulation, softcap and cross entropy
- *    in fp32, rows at or past unpadded_vocab_size never enter the softmax, an
- *    fp32 head is rounded to bf16.
+ *    a bf16 x bf16 projection accumulated in fp32, then the softcap and the
+ *    loss in fp32 arithmetic; only head rows below unpadded_vocab_size take
+ *    part in the softmax; an fp32 head takes part through its bf16 rounding.
  *  - "nemo_automodel.components.loss.linear_ce", FusedLinearCrossEntropy
  *    (constructor: ignore_index, logit_softcapping, reduction; forward:
  *    hidden_states, labels, lm_weight, num_label_tokens; scalar result).
@@ -33,8 +33,10 @@
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers on the current HIP device,
  *    row-major and contiguous.  The caller owns every buffer; the library
- *    allocates no device memory and keeps no state between calls.  Inputs
- *    are read only.
+ *    allocates no device memory, and no compute call carries state to the
+ *    next one.  The one process-wide state is the launch trace
+ *    (flce_trace_*, for measurement): while it runs, every launch also
+ *    records a pair of HIP events into it.  Inputs are read only.
  *  - Work is enqueued on `stream` and the call returns without waiting for
  *    it (no host synchronisation).
  *  - The return value is an flce_status_t.  Argument errors are detected on
@@ -102,10 +104,10 @@ typedef enum flce_dtype {
  *                   num_label_tokens); < 0: not given.  0 is invalid.
  * weight_dtype      FLCE_DTYPE_BF16, or FLCE_DTYPE_FP32 for an fp32 head that
  *                   each call rounds to bf16 itself (Inkling2 page, class
- *                   description: an FP32 head is rounded to BF16, the cast
- *                   FSDP applies).  The rounded copy of rows < Vu is staged
- *                   in the workspace, which grows by Vu*Hp*2 bytes; rows >= Vu
- *                   are never read.
+ *                   description: an fp32 head is used at its bf16 value,
+ *                   rounded to nearest even like torch's cast).  The rounded
+ *                   copy of rows < Vu is staged in the workspace, which grows
+ *                   by Vu*Hp*2 bytes; rows >= Vu are never read.
  */
 typedef struct flce_problem {
   int64_t num_tokens;
@@ -176,8 +178,8 @@ int flce_backward(const flce_problem_t* problem, const void* hidden, const void*
 /*
  * Round an fp32 head to the bf16 compute copy the kernels read: nearest
  * value, ties to even, NaN stays NaN ("nemo_automodel.components.models.
- * inkling2.loss", class description: an FP32 head is rounded to BF16, the
- * cast FSDP applies).
+ * inkling2.loss", class description: an fp32 head is used at its bf16
+ * value, the rounding sharded training applies to the model's own head).
  *
  * src    fp32 [count], 4-byte aligned (device).
  * dst    bf16 [count], 2-byte aligned (device); may not overlap src.

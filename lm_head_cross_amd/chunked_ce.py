@@ -15,7 +15,7 @@ import ctypes
 import torch
 
 from . import _lib
-from .flce import _need, _ptr, _raise_for, _stream_ptr
+from .flce import _need, _ptr, _raise_for, _stream_ptr, raise_for_device_status
 
 _REDUCTIONS = {"sum": _lib.FLCE_REDUCTION_SUM, "mean": _lib.FLCE_REDUCTION_MEAN}
 _DTYPES = {torch.bfloat16: _lib.FLCE_DTYPE_BF16, torch.float32: _lib.FLCE_DTYPE_FP32}
@@ -123,14 +123,17 @@ def chunked_ce_mask_labels(labels, mask, ignore_index: int = -100, stream=None) 
 
 class _ChunkedCE(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, logits2d, labels1d, ignore_index, reduction, num_label_tokens, chunk_len):
+    def forward(ctx, logits2d, labels1d, ignore_index, reduction, num_label_tokens, chunk_len, check_labels):
         T, V = logits2d.shape
         problem = make_ce_problem(T, V, logits2d.dtype, ignore_index, reduction, num_label_tokens, chunk_len)
         dev = logits2d.device
         ws = alloc_ce_workspace(problem, dev)
         loss = torch.empty((), dtype=torch.float32, device=dev)
         lse = torch.empty(T, dtype=torch.float32, device=dev)
-        chunked_ce_forward(problem, logits2d, labels1d, loss, lse, workspace=ws)
+        status = torch.zeros((), dtype=torch.int32, device=dev) if check_labels else None
+        chunked_ce_forward(problem, logits2d, labels1d, loss, lse, device_status=status, workspace=ws)
+        if check_labels:
+            raise_for_device_status(status, "cross entropy")
         ctx.save_for_backward(logits2d, labels1d, lse)
         ctx.problem = problem
         return loss
@@ -141,10 +144,10 @@ class _ChunkedCE(torch.autograd.Function):
         g = grad_out.detach().to(torch.float32).contiguous()
         d = torch.empty_like(logits2d)
         chunked_ce_backward(ctx.problem, logits2d, labels1d, lse, g, d)
-        return d, None, None, None, None, None
+        return d, None, None, None, None, None, None
 
 
-def _apply(logits, labels, mask, ignore_index, reduction, num_label_tokens, chunk_len):
+def _apply(logits, labels, mask, ignore_index, reduction, num_label_tokens, chunk_len, check_labels=True):
     if logits.dim() < 1:
         raise ValueError("logits must have a vocabulary dimension")
     V = logits.shape[-1]
@@ -166,13 +169,15 @@ def _apply(logits, labels, mask, ignore_index, reduction, num_label_tokens, chun
     if lab.dtype != torch.int64:
         lab = lab.to(torch.int64)
     return _ChunkedCE.apply(logits.reshape(-1, V).contiguous(), lab.contiguous(), int(ignore_index), reduction,
-                            num_label_tokens, int(chunk_len))
+                            num_label_tokens, int(chunk_len), bool(check_labels))
 
 
-def compute_cross_entropy(logits, targets, ignore_index=-100, reduction="sum"):
+def compute_cross_entropy(logits, targets, ignore_index=-100, reduction="sum", check_labels=True):
     """Cross-entropy of ``logits`` (sequence, classes) against ``targets``
-    (sequence,); the sum of the per-position losses for 'sum'."""
-    return _apply(logits, targets, None, ignore_index, reduction, None, 32)
+    (sequence,); the sum of the per-position losses for 'sum'.  A target
+    outside [0, classes) that is not ignore_index raises ValueError unless
+    ``check_labels`` is off (then it is skipped like an ignored one)."""
+    return _apply(logits, targets, None, ignore_index, reduction, None, 32, check_labels)
 
 
 class ChunkedCrossEntropy(torch.nn.Module):
@@ -182,11 +187,13 @@ class ChunkedCrossEntropy(torch.nn.Module):
 
     ``chunk_len`` must be positive; the kernels never hold an fp32 copy of the
     logits, so it bounds nothing further.  ``compile`` is accepted for the
-    signature: the kernels are compiled ahead of time.
+    signature: the kernels are compiled ahead of time.  ``check_labels``
+    (default on) raises ValueError for a kept label outside [0, vocab) that
+    is not ignore_index (one host read per forward).
     """
 
     def __init__(self, chunk_len: int = 32, compile: bool = True, ignore_index: int = -100,
-                 reduction: str = "sum"):
+                 reduction: str = "sum", check_labels: bool = True):
         super().__init__()
         if int(chunk_len) <= 0:
             raise ValueError("chunk_len must be positive")
@@ -196,6 +203,8 @@ class ChunkedCrossEntropy(torch.nn.Module):
         self.compile = bool(compile)
         self.ignore_index = ignore_index
         self.reduction = reduction
+        self.check_labels = bool(check_labels)
 
     def forward(self, logits, labels, mask=None, num_label_tokens=None):
-        return _apply(logits, labels, mask, self.ignore_index, self.reduction, num_label_tokens, self.chunk_len)
+        return _apply(logits, labels, mask, self.ignore_index, self.reduction, num_label_tokens, self.chunk_len,
+                      self.check_labels)

@@ -127,6 +127,9 @@ struct Online {
       s *= __builtin_amdgcn_exp2f(m2 - g2);
       m2 = g2;
     }
+    // Everything seen so far is -inf (masked columns): nothing to add, and
+    // x - m2 would be -inf + inf.
+    if (m2 == kNegInf) return;
     float a = 0.0f;
 #pragma unroll
     for (int i = 0; i < N; ++i) a += __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], kLog2e, -m2));

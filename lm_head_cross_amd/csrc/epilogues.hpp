@@ -13,9 +13,10 @@ using gemm::acc_row;
 // Forward: logits tile z^T (rows = head rows v, columns = compacted tokens t).
 // Applies the softcap, drops rows v >= Vu, and reduces each token column to a
 // (max, sum exp(z' - max)) pair for this vocab tile; the tile that holds a
-// token's label also records z'[t, y_t].  (Inkling2 loss page, class
-// description: softcap and cross entropy in fp32, rows past the usable
-// vocabulary never enter the softmax.)
+// token's label also records z'[t, y_t].  ("nemo_automodel.components.
+// models.inkling2.loss", class description: the softcap and the loss are fp32
+// arithmetic, and only head rows below unpadded_vocab_size take part in the
+// softmax.)
 //
 // MB: MFMA blocks per wave along the head rows (4 for the 256-row tile, 6
 // for the 384-row one); the waves' two rows of 32*MB head rows are merged

@@ -461,8 +461,8 @@ void zero_fill(void* p, int64_t bytes, hipStream_t s) {
 // The bf16 head the kernels read, rows of Hp elements: the caller's for a
 // bf16 head with H a multiple of 128; otherwise its rows < Vu copied into
 // the workspace, an fp32 head rounded to nearest even ("nemo_automodel.
-// components.models.inkling2.loss", class description: an fp32 head is
-// rounded to bf16 with the cast FSDP applies), with zero columns H..Hp.
+// components.models.inkling2.loss", class description: an fp32 head is used
+// at its bf16 value), with zero columns H..Hp.
 // Rows >= Vu are never read.
 const bf16* staged_head(const Plan& pl, const flce_problem_t& p, const void* weight, void* workspace,
                         hipStream_t stream) {

@@ -203,10 +203,19 @@ class LaunchTrace:
 # ---------------------------------------------------------------------------
 
 
+def raise_for_device_status(status: torch.Tensor, what: str) -> None:
+    """Raise ValueError if the device status word reports a label outside
+    [0, unpadded vocabulary) that is not ignore_index (waits for the stream
+    that wrote it)."""
+    if int(status.item()) & _lib.FLCE_DEVICE_BAD_LABEL:
+        raise ValueError(f"{what}: a label is neither ignore_index nor inside [0, unpadded vocabulary) "
+                         "(PyTorch's cross entropy rejects such a target)")
+
+
 class _FusedLinearCE(torch.autograd.Function):
     @staticmethod
     def forward(ctx, hidden, weight, labels, unpadded_vocab, softcap, ignore_index, reduction,
-                num_label_tokens):
+                num_label_tokens, check_labels):
         T, H = hidden.shape
         problem = make_problem(T, H, weight.shape[0], unpadded_vocab, softcap, ignore_index, reduction,
                                num_label_tokens)
@@ -217,7 +226,10 @@ class _FusedLinearCE(torch.autograd.Function):
         ws = alloc_workspace(problem, dev)
         loss = torch.empty((), dtype=torch.float32, device=dev)
         lse = torch.empty(T, dtype=torch.float32, device=dev)
-        flce_forward(problem, hidden, weight, labels, loss, lse, workspace=ws)
+        status = torch.zeros((), dtype=torch.int32, device=dev) if check_labels else None
+        flce_forward(problem, hidden, weight, labels, loss, lse, device_status=status, workspace=ws)
+        if check_labels:
+            raise_for_device_status(status, "fused linear cross entropy")
         ctx.save_for_backward(hidden, weight, labels, lse)
         ctx.problem = problem
         return loss
@@ -232,17 +244,21 @@ class _FusedLinearCE(torch.autograd.Function):
         flce_backward(problem, hidden, weight, labels, lse, g, d_hidden, d_weight)
         # The bf16 rounding of an fp32 head passes the gradient through, so
         # d_weight is already the fp32 head's gradient.
-        return d_hidden, d_weight, None, None, None, None, None, None
+        return d_hidden, d_weight, None, None, None, None, None, None, None
 
 
 def fused_linear_cross_entropy(hidden_states, labels, lm_weight, unpadded_vocab_size=None,
                                logit_softcapping=0.0, ignore_index=-100, reduction="sum",
-                               num_label_tokens=None):
+                               num_label_tokens=None, check_labels=True):
     """Loss of ``hidden_states`` [..., H] against ``lm_weight`` [V, H].
 
-    An fp32 head is rounded to bf16 (round to nearest even) by the library
-    before the projection, as the Inkling2 loss page describes; the fp32
-    head receives the fp32 gradient.
+    An fp32 head takes part through its bf16 value (round to nearest even,
+    done by the library), per the Inkling2 loss page; the fp32 head receives
+    the fp32 gradient.  With ``check_labels`` (the default) a label that is
+    neither ignore_index nor inside the usable vocabulary raises ValueError,
+    as PyTorch's cross entropy does; the check reads the library's device
+    status word once, which waits for the forward pass.  With it off, such a
+    position is skipped like an ignored one.
     """
     H = hidden_states.shape[-1]
     hidden = hidden_states.reshape(-1, H)
@@ -258,7 +274,7 @@ def fused_linear_cross_entropy(hidden_states, labels, lm_weight, unpadded_vocab_
         lab = lab.to(torch.int64)
     return _FusedLinearCE.apply(hidden.contiguous(), w.contiguous(), lab.contiguous(),
                                 unpadded_vocab_size, float(logit_softcapping), int(ignore_index),
-                                reduction, num_label_tokens)
+                                reduction, num_label_tokens, bool(check_labels))
 
 
 class FusedLinearCrossEntropy(torch.nn.Module):
@@ -271,10 +287,12 @@ class FusedLinearCrossEntropy(torch.nn.Module):
     row) restricts the softmax to the first rows, as on the Inkling2 page.
     The head's gradient is computed in fp32 and handed to autograd, which
     gives a bf16 head a bf16 gradient and an fp32 head the fp32 one.
+    ``check_labels`` (default on) raises ValueError for a label outside the
+    usable vocabulary that is not ignore_index (one host read per forward).
     """
 
     def __init__(self, ignore_index: int = -100, logit_softcapping: float = 0, reduction: str = "sum",
-                 unpadded_vocab_size: int | None = None):
+                 unpadded_vocab_size: int | None = None, check_labels: bool = True):
         super().__init__()
         if reduction not in _REDUCTIONS:
             raise ValueError(f"reduction must be one of {sorted(_REDUCTIONS)}")
@@ -286,6 +304,7 @@ class FusedLinearCrossEntropy(torch.nn.Module):
         self.logit_softcapping = logit_softcapping
         self.reduction = reduction
         self.unpadded_vocab_size = None if unpadded_vocab_size is None else int(unpadded_vocab_size)
+        self.check_labels = bool(check_labels)
 
     @staticmethod
     def materialize_lm_weight(lm_weight, grad_reduce_group=None):
@@ -302,7 +321,7 @@ class FusedLinearCrossEntropy(torch.nn.Module):
         w = self.materialize_lm_weight(lm_weight, grad_reduce_group)
         return fused_linear_cross_entropy(hidden_states, labels, w, self.unpadded_vocab_size,
                                           self.logit_softcapping, self.ignore_index, self.reduction,
-                                          num_label_tokens)
+                                          num_label_tokens, self.check_labels)
 
 
 class Inkling2FusedLinearCrossEntropy(FusedLinearCrossEntropy):
@@ -310,7 +329,7 @@ class Inkling2FusedLinearCrossEntropy(FusedLinearCrossEntropy):
     head rows (Inkling2 loss page; softcap default 30)."""
 
     def __init__(self, unpadded_vocab_size: int, logit_softcapping: float = 30.0, ignore_index: int = -100,
-                 reduction: str = "sum"):
+                 reduction: str = "sum", check_labels: bool = True):
         if unpadded_vocab_size is None:
             raise ValueError("unpadded_vocab_size is required")
-        super().__init__(ignore_index, logit_softcapping, reduction, unpadded_vocab_size)
+        super().__init__(ignore_index, logit_softcapping, reduction, unpadded_vocab_size, check_labels)

@@ -114,3 +114,46 @@ def test_module_backward_matches_oracle(name):
     ignored = (y == -100).to(d)
     assert torch.all(Xd.grad[ignored] == 0)
     assert torch.all(Wd.grad[vu:] == 0)
+
+
+@pytest.mark.gpu
+def test_module_rejects_label_outside_usable_vocabulary():
+    """A label in [Vu, V) or negative (not ignore_index) raises ValueError by
+    default, as PyTorch's cross entropy does; with check_labels off the
+    position is skipped like an ignored one (the oracle's loss without it)."""
+    import oracle
+
+    d = torch.device("cuda:0")
+    X, W, y = _inputs(5, 1, 200, 128, 1100, 1000, 0.1, torch.bfloat16)
+    for bad_label in (1000, 1099, -3):
+        yb = y.clone()
+        yb[0, 17] = bad_label
+        with pytest.raises(ValueError):
+            L.FusedLinearCrossEntropy(unpadded_vocab_size=1000)(X.to(d), yb.to(d), W.to(d))
+        with pytest.raises(ValueError):
+            L.Inkling2FusedLinearCrossEntropy(1000)(X.to(d), yb.to(d), W.to(d))
+    yb = y.clone()
+    yb[0, 17] = 1050
+    loss = L.FusedLinearCrossEntropy(unpadded_vocab_size=1000, check_labels=False)(X.to(d), yb.to(d), W.to(d))
+    yr = y.clone()
+    yr[0, 17] = -100
+    ref = oracle.forward(oracle.to_f64(X.reshape(-1, 128)), oracle.head_values(W), yr.reshape(-1).numpy(),
+                         oracle.Problem(1000))
+    assert abs(loss.item() - ref.loss) <= 1e-4 * abs(ref.loss)
+
+
+@pytest.mark.gpu
+def test_chunked_module_rejects_label_outside_vocabulary():
+    d = torch.device("cuda:0")
+    g = torch.Generator().manual_seed(9)
+    z = torch.randn(50, 300, generator=g).to(d)
+    y = torch.randint(0, 300, (50,), generator=g).to(d)
+    y[3] = 300
+    with pytest.raises(ValueError):
+        L.ChunkedCrossEntropy()(z, y)
+    with pytest.raises(ValueError):
+        L.compute_cross_entropy(z, y)
+    loss = L.ChunkedCrossEntropy(check_labels=False)(z, y)
+    yr = y.clone()
+    yr[3] = -100
+    assert abs(loss.item() - L.compute_cross_entropy(z, yr).item()) <= 1e-5 * abs(loss.item())

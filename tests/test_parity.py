@@ -14,8 +14,8 @@ import pytest
 import torch
 
 import oracle
-from tests.gpu_common import (TOL_GRAD_REL_L2, TOL_TOKEN_ABS, TOL_TOTAL_REL, check_full, oracle_problem,
-                              rel_l2, run_hip, say, stored_lse)
+from tests.gpu_common import (TOL_GRAD_REL_L2, TOL_TOKEN_ABS, TOL_TOTAL_REL, check_full, check_rows,
+                              oracle_problem, rel_l2, run_hip, say, stored_lse)
 from workloads import WORKLOADS, Workload, make_inputs, sample_rows
 
 pytestmark = pytest.mark.gpu
@@ -50,6 +50,10 @@ SMALL = {
     "vocab_384": _small(109, T=260, H=128, V=384, Vu=384, w_std=0.2, softcap=15.0, ignore_frac=0.05),
     "vocab_400": _small(110, T=300, H=256, V=420, Vu=400, w_std=0.2, ignore_frac=0.05),
     "vocab_383": _small(111, T=200, H=128, V=383, Vu=383, w_std=0.2, ignore_frac=0.05),
+    # fewer than 384 usable rows with a softcap: the 256-row softcapped
+    # forward and recompute tiles, a straddling tile and NaN-free padding
+    "vocab_300_softcap": _small(112, T=300, H=128, V=383, Vu=300, w_std=0.5, pad_std=30.0, softcap=30.0,
+                                ignore_frac=0.05),
 }
 
 
@@ -297,9 +301,9 @@ def test_workload_full_size(key):
     p = oracle_problem(inp)
     D = oracle.divisor(p, int(valid.sum()))
     lse_all = stored_lse(key)
-    ll = oracle.label_logits(X, W, y, p)
-    ref_tl = np.where(valid, lse_all - ll, 0.0)
-    ref_loss = math.fsum(ref_tl.tolist()) / D
+    ref = oracle.loss_from_lse(lse_all, oracle.label_logits(X, W, y, p), y, p)
+    ref_tl, ref_loss = ref.token_loss, ref.loss
+    assert ref.D == D
     tl_err = np.abs(res["token_loss"].double().numpy() - ref_tl).max()
     say(f"  loss gpu={res['loss']:.9g} ref={ref_loss:.9g} rel={abs(res['loss'] - ref_loss) / abs(ref_loss):.3g}"
         f" max|dl|={tl_err:.3g}")
@@ -318,6 +322,9 @@ def test_workload_full_size(key):
     say(f"  dX relL2 over {len(tok)} rows = {e_dx:.3g}; dW relL2 over {len(voc)} rows = {e_dw:.3g}")
     assert e_dx <= TOL_GRAD_REL_L2
     assert e_dw <= TOL_GRAD_REL_L2
+    wx = check_rows(res["dX"].double().numpy(), dX_s, "dX")
+    ww = check_rows(res["dW"].double().numpy(), dW_r, "dW")
+    say(f"  worst row error / row scale: dX {wx:.3g}, dW {ww:.3g}")
 
 
 def test_no_logits_sized_allocation():
