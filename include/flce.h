@@ -159,6 +159,30 @@ int flce_forward(const flce_problem_t* problem, const void* hidden, const void* 
                  hipStream_t stream);
 
 /*
+ * Forward pass without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving or
+ * scoring loops, harnesses that forbid allocation).  Same arguments and
+ * results as flce_forward, bit for bit, but the scratch is the library's own
+ * fixed array of 64 MiB per device (device memory that the library's code
+ * object brings, held until the process ends); the call allocates nothing.
+ *
+ * Limit: the forward's scratch must fit the 64 MiB, about
+ *   Tp*Hp*2 + ceil(Vu/256)*Tp*8 + 13*Tp + 1 KiB   bytes
+ * with Tp = T rounded up to 256 and Hp = H rounded up to 128, plus Vu*Hp*2
+ * when the head is staged (an fp32 head, or H not a multiple of 128).  The
+ * llama3-8b head at T = 4096 (H = 4096, V = 128256) needs 48 MiB.  A larger
+ * problem returns FLCE_ERR_WORKSPACE before anything is launched.
+ * FLCE_ERR_HIP if the scratch's device address cannot be looked up.
+ *
+ * Every call on one device shares that device's scratch: calls that overlap
+ * in time on one device (several streams or host threads) race and give
+ * wrong results.  Nothing in the scratch needs to start at zero.
+ */
+int flce_forward_noalloc(const flce_problem_t* problem, const void* hidden, const void* weight,
+                         const int64_t* labels, float* loss, float* lse, float* token_loss,
+                         int32_t* device_status, hipStream_t stream);
+
+/*
  * Backward pass: gradients of grad_out * loss.
  *
  * hidden, weight, labels   as passed to flce_forward.

@@ -22,7 +22,8 @@ FLCE_REDUCTION_MEAN = 1
 FLCE_DTYPE_BF16 = 0
 FLCE_DTYPE_FP32 = 1
 
-EXPORTED = ("flce_status_string", "flce_version", "flce_workspace_size", "flce_forward", "flce_backward",
+EXPORTED = ("flce_status_string", "flce_version", "flce_workspace_size", "flce_forward", "flce_forward_noalloc",
+            "flce_backward",
             "flce_round_to_bf16", "flce_trace_start", "flce_trace_select", "flce_trace_stop", "flce_trace_count", "flce_trace_get",
             "chunked_ce_workspace_size", "chunked_ce_forward", "chunked_ce_backward", "chunked_ce_mask_labels")
 
@@ -86,6 +87,8 @@ def load() -> ctypes.CDLL:
     lib.flce_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
     lib.flce_forward.restype = ctypes.c_int
     lib.flce_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.flce_forward_noalloc.restype = ctypes.c_int
+    lib.flce_forward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.flce_backward.restype = ctypes.c_int
     lib.flce_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.flce_trace_start.restype = ctypes.c_int

@@ -16,6 +16,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "../../include/flce.h"
@@ -300,6 +301,7 @@ struct Plan {
   size_t off_wst;       // the staged head [Vu, Hp] bf16 (0 bytes when the caller's head is read directly)
   size_t off_part;      // forward region
   size_t off_g, off_hacc, off_xct;  // backward region
+  size_t fwd_total;     // bytes the forward pass touches (a prefix of the workspace)
   size_t total;
 };
 
@@ -431,6 +433,7 @@ Plan make_plan(const flce_problem_t* p, int n_cu = 256) {
   pl.off_hacc = take(pl.tiles_v > 1 ? pl.Tvp * pl.H * 4 : 0);
   pl.off_xct = take(pl.Tvp * pl.Hp * 2);
   const size_t bwd_end = o;
+  pl.fwd_total = fwd_end;
   pl.total = std::max(fwd_end, bwd_end);
   return pl;
 }
@@ -498,6 +501,37 @@ void launch_compact_gather(const Plan& pl, const flce_problem_t& p, const int64_
                      (uint4*)xc, pl.Tvp);
 }
 
+// The no-allocation forward's scratch (flce_forward_noalloc): device memory
+// of fixed size that the code object brings, one copy per device, held until
+// the process ends.  Its name is a host-side stand-in: host code uses only
+// the per-device address hipGetSymbolAddress returns.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+
+}  // namespace
+}  // namespace flce
+
+static __device__ __align__(256) unsigned char scratch[flce::kStaticScratchBytes];
+
+namespace flce {
+namespace {
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; nullptr if the lookup fails.
+void* static_scratch_ptr() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
+}
+
 }  // namespace
 }  // namespace flce
 
@@ -542,9 +576,21 @@ int flce_workspace_size(const flce_problem_t* problem, size_t* bytes) {
   return FLCE_OK;
 }
 
-int flce_forward(const flce_problem_t* problem, const void* hidden, const void* weight, const int64_t* labels,
+}  // extern "C"
+
+namespace flce {
+namespace {
+
+// Which scratch the forward pass runs in.
+enum class ScratchSource { kCallerWorkspace, kStaticScratch };
+
+void* static_scratch_ptr();
+
+// The forward pass on a caller's workspace (which must hold both passes'
+// bytes) or on the library's static scratch (which must hold the forward's).
+int forward_impl(const flce_problem_t* problem, const void* hidden, const void* weight, const int64_t* labels,
                  float* loss, float* lse, float* token_loss, int32_t* device_status, void* workspace,
-                 size_t workspace_bytes, hipStream_t stream) {
+                 size_t workspace_bytes, hipStream_t stream, ScratchSource src) {
   int st = validate(problem);
   if (st != FLCE_OK) return st;
   const flce_problem_t& p = *problem;
@@ -559,7 +605,13 @@ int flce_forward(const flce_problem_t* problem, const void* hidden, const void* 
     return launch_status();
   }
   const Plan pl = make_plan(&p);
-  if ((st = check_workspace(pl, workspace, workspace_bytes)) != FLCE_OK) return st;
+  if (src == ScratchSource::kStaticScratch) {
+    if (pl.fwd_total > kStaticScratchBytes) return FLCE_ERR_WORKSPACE;
+    workspace = static_scratch_ptr();
+    if (!workspace) return FLCE_ERR_HIP;
+  } else if ((st = check_workspace(pl, workspace, workspace_bytes)) != FLCE_OK) {
+    return st;
+  }
 
   Meta* meta = ws_at<Meta>(workspace, pl.off_meta);
   int32_t* valid_idx = ws_at<int32_t>(workspace, pl.off_valid);
@@ -615,6 +667,25 @@ int flce_forward(const flce_problem_t* problem, const void* hidden, const void* 
                        (const Meta*)meta, (int)p.reduction, p.num_label_tokens, loss);
   }
   return launch_status();
+}
+
+}  // namespace
+}  // namespace flce
+
+extern "C" {
+
+int flce_forward(const flce_problem_t* problem, const void* hidden, const void* weight, const int64_t* labels,
+                 float* loss, float* lse, float* token_loss, int32_t* device_status, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream) {
+  return forward_impl(problem, hidden, weight, labels, loss, lse, token_loss, device_status, workspace,
+                      workspace_bytes, stream, ScratchSource::kCallerWorkspace);
+}
+
+int flce_forward_noalloc(const flce_problem_t* problem, const void* hidden, const void* weight,
+                         const int64_t* labels, float* loss, float* lse, float* token_loss,
+                         int32_t* device_status, hipStream_t stream) {
+  return forward_impl(problem, hidden, weight, labels, loss, lse, token_loss, device_status, nullptr, 0, stream,
+                      ScratchSource::kStaticScratch);
 }
 
 int flce_backward(const flce_problem_t* problem, const void* hidden, const void* weight, const int64_t* labels,

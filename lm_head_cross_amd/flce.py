@@ -119,6 +119,28 @@ def flce_forward(problem, hidden, weight, labels, loss, lse, token_loss=None, de
     _raise_for(code, "flce_forward")
 
 
+def flce_forward_noalloc(problem, hidden, weight, labels, loss, lse, token_loss=None, device_status=None,
+                         stream=None) -> None:
+    """Enqueue the forward pass on the library's fixed per-device scratch (no
+    workspace, nothing allocated); see include/flce.h for the size limit and
+    the rule that calls overlapping on one device race."""
+    T, H, V = problem.num_tokens, problem.hidden, problem.vocab
+    dev = weight.device
+    _need(weight, "weight", _weight_dtype(problem), (V, H), dev)
+    _need(hidden, "hidden", torch.bfloat16, (T, H), dev)
+    _need(labels, "labels", torch.int64, (T,), dev)
+    _need(loss, "loss", torch.float32, (), dev)
+    _need(lse, "lse", torch.float32, (T,), dev)
+    if token_loss is not None:
+        _need(token_loss, "token_loss", torch.float32, (T,), dev)
+    if device_status is not None:
+        _need(device_status, "device_status", torch.int32, (), dev)
+    code = _lib.load().flce_forward_noalloc(
+        ctypes.byref(problem), _ptr(hidden), _ptr(weight), _ptr(labels), _ptr(loss), _ptr(lse),
+        _ptr(token_loss), _ptr(device_status), _stream_ptr(stream))
+    _raise_for(code, "flce_forward_noalloc")
+
+
 def flce_backward(problem, hidden, weight, labels, lse, grad_out, d_hidden, d_weight, device_status=None,
                   workspace=None, stream=None) -> None:
     """Enqueue the backward pass; see include/flce.h for the contract."""
