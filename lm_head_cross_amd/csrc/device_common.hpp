@@ -32,16 +32,16 @@ __device__ __forceinline__ float exp_e(float x) { return __builtin_amdgcn_exp2f(
 // Natural log through the hardware base-2 logarithm.
 __device__ __forceinline__ float log_e(float x) { return __builtin_amdgcn_logf(x) * kLn2; }
 
-// Logit softcap z' = c tanh(z / c) (Inkling2 loss page, class description:
-// the softcap is applied in fp32).  tanh(y) is evaluated as
-// sign(y) (1 - e) / (1 + e) with e = exp(-2|y|) in (0, 1], which cannot
-// overflow; its absolute error is a few fp32 ulps of 1, i.e. about 2e-6 in z'
-// for c = 30.
-__device__ __forceinline__ float softcap_apply(float z, float c, float inv_c) {
-  const float y = z * inv_c;
-  const float e = __builtin_amdgcn_exp2f(-2.0f * kLog2e * __builtin_fabsf(y));
-  const float t = (1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e);
-  return __builtin_copysignf(c * t, y);
+// Logit softcap z' = c tanh(z / c) ("nemo_automodel.components.models.
+// inkling2.loss", class description: the softcap is fp32 arithmetic).
+// tanh(y) = 1 - 2 / (1 + e^{2y}), with e^{2y} from the hardware base-2
+// exponential (k2 = 2 log2(e) / c) and one hardware reciprocal: for y > 44,
+// e^{2y} = inf and the quotient is 0 (tanh = 1); for y < -44 it is 2
+// (tanh = -1).  The absolute error is a few fp32 ulps of 1, about 2e-6 in
+// z' for c = 30.  softcap_recip returns 1 / (1 + e^{2y}); the epilogues fold
+// the rest (c (1 - 2 r), or 1 - 2 r) into one fma.
+__device__ __forceinline__ float softcap_recip(float z, float k2) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * k2));
 }
 
 // Merge two (max, sum of exp(x - max)) pairs; a max of -inf means "empty".

@@ -57,6 +57,8 @@ struct Lse {
     float* xchg = reinterpret_cast<float*>(smem);  // [2][256][4]
     const bool ragged = a0 < m0 || a0 + kTileRows > p.vocab_limit;
     const int row0 = a0 + wm * kWaveRows;   // head row of this wave's first accumulator row
+    const float k2 = 2.0f * kLog2e * p.inv_softcap;
+    const float c = p.softcap;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const int tc = acc_col(wn, nb, lane);
@@ -74,7 +76,7 @@ struct Lse {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float v = acc[mb][nb][r];
-          if constexpr (CAP) v = softcap_apply(v, p.softcap, p.inv_softcap);
+          if constexpr (CAP) v = __builtin_fmaf(softcap_recip(v, k2), -2.0f * c, c);  // c tanh(z / c)
           z[r] = v;
         }
         if (ragged) {
@@ -145,6 +147,14 @@ struct Lse {
 // rounded to bf16 and stored token-major, G[t][v - chunk start].  Positions
 // past the valid tokens or the chunk get 0.  (chunked_ce page,
 // _ChunkedCrossEntropySum.backward: the fp32 softmax is recomputed.)
+//
+// The epilogue runs while no MFMA issues, so its per-logit work is kept to
+// the minimum: exp(z' - lse) is one fma into the base-2 exponential; g/D
+// and the token mask are one per-column factor (0 past the valid tokens);
+// with the softcap, t = tanh(z/c) is one exponential, one reciprocal and one
+// fma, z' - lse = c t - lse one fma, and the slope 1 - t^2 another.  The
+// one-hot term is subtracted only in the columns whose label falls into the
+// wave's rows (a wave-uniform branch, about 5% of columns at V = 128256).
 template <bool CAP, int MB = 4>
 struct Grad {
   struct Params {
@@ -166,6 +176,49 @@ struct Grad {
     apply(p, acc, m0, m0, n0, smem);
   }
 
+  // One token column of the wave's accumulators (column block nb): its
+  // 16 * MB values, stored from chunk row m0 on.  LABEL: the column's label
+  // may fall into these rows (y_rel: label row relative to row0).
+  template <bool LABEL, int nb>
+  static __device__ __forceinline__ void column(const Params& p, const f32x16 (&acc)[MB][4], int hi,
+                                                int row0, int m0, bool shifted, int y_rel, float nl2, float st,
+                                                float k2, float cl2, bf16* grow) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        bf16x4 out;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rel = 32 * mb + 8 * q + 4 * hi + i;   // row within the wave's rows
+          const float z = acc[mb][nb][4 * q + i];
+          float g;
+          if constexpr (CAP) {
+            const float t = __builtin_fmaf(-2.0f, softcap_recip(z, k2), 1.0f);  // tanh(z / c)
+            float d = __builtin_amdgcn_exp2f(__builtin_fmaf(t, cl2, nl2));       // exp(z' - lse)
+            if constexpr (LABEL) d -= rel == y_rel ? 1.0f : 0.0f;
+            g = d * (__builtin_fmaf(-t, t, 1.0f) * st);
+          } else {
+            float d = __builtin_amdgcn_exp2f(__builtin_fmaf(z, kLog2e, nl2));
+            if constexpr (LABEL) d -= rel == y_rel ? 1.0f : 0.0f;
+            g = d * st;
+          }
+          // A 256-row tile can reach past the chunk's last row (a 384-row
+          // tile is shifted to end there).
+          if constexpr (MB == 4) g = row0 + rel < p.vw ? g : 0.0f;
+          out[i] = (bf16)g;
+        }
+        const int mq = row0 + 32 * mb + 8 * q + 4 * hi;
+        if (!shifted) {
+          *reinterpret_cast<bf16x4*>(grow + mq) = out;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (mq + i >= m0) grow[mq + i] = out[i];
+        }
+      }
+  }
+
   // m0: the tile's first chunk row; a0 <= m0: the chunk row of accumulator
   // row 0.  A tile computed shifted down (a0 < m0) ends at the chunk's last
   // row and stores only its rows from m0 on, one value at a time; the rows
@@ -175,46 +228,37 @@ struct Grad {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
+    const int hi = lane >> 5;
     const int tv = *p.tok_count;  // > 0: tiles past the valid tokens never get here
     const float scale = *p.scale;
     const bool shifted = a0 < m0;
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int t = n0 + acc_col(wn, nb, lane);
-      const bool tok_ok = t < tv;
-      const int ts = tok_ok ? t : 0;
-      const float lse_t = p.lse[p.valid_idx[ts]];
-      const int y_loc = tok_ok ? p.yc[ts] - p.v0 : -1;
-      bf16* grow = p.G + (int64_t)t * p.ldg;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          bf16x4 out;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 4 * q + i;
-            const int m = a0 + wm * kWaveRows + 32 * mb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            float z = acc[mb][nb][r];
-            if constexpr (CAP) z = softcap_apply(z, p.softcap, p.inv_softcap);
-            float d = exp_e(z - lse_t) - (m == y_loc ? 1.0f : 0.0f);
-            if constexpr (CAP) {
-              const float u = z * p.inv_softcap;
-              d *= 1.0f - u * u;
-            }
-            out[i] = (bf16)((tok_ok && m < p.vw) ? d * scale : 0.0f);
-          }
-          const int mq = a0 + wm * kWaveRows + 32 * mb + 8 * q + 4 * (lane >> 5);
-          if (!shifted) {
-            *reinterpret_cast<bf16x4*>(grow + mq) = out;
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (mq + i >= m0) grow[mq + i] = out[i];
-          }
-        }
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    const int row0 = a0 + wm * kWaveRows;
+    const float k2 = 2.0f * kLog2e * p.inv_softcap;
+    const float cl2 = p.softcap * kLog2e;
+    columns<0>(p, acc, wn, lane, hi, n0, tv, scale, row0, m0, shifted, k2, cl2);
+  }
+
+  // Token column blocks nb, nb+1, .. 3 (a compile-time index, so that the
+  // accumulators stay in registers).
+  template <int nb>
+  static __device__ __forceinline__ void columns(const Params& p, const f32x16 (&acc)[MB][4], int wn, int lane,
+                                                 int hi, int n0, int tv, float scale, int row0, int m0, bool shifted,
+                                                 float k2, float cl2) {
+    const int t = n0 + acc_col(wn, nb, lane);
+    const bool tok_ok = t < tv;
+    const int ts = tok_ok ? t : 0;
+    const float nl2 = -p.lse[p.valid_idx[ts]] * kLog2e;
+    const float st = tok_ok ? scale : 0.0f;
+    const int y_rel = tok_ok ? p.yc[ts] - p.v0 - row0 : -1;
+    // The lane holding the label's row: rows 8k + 4 hi + 0..3 of the wave's.
+    const bool own = (unsigned)y_rel < (unsigned)kWaveRows && ((y_rel >> 2) & 1) == hi;
+    bf16* grow = p.G + (int64_t)t * p.ldg;
+    if (__builtin_amdgcn_ballot_w64(own) != 0)
+      column<true, nb>(p, acc, hi, row0, m0, shifted, y_rel, nl2, st, k2, cl2, grow);
+    else
+      column<false, nb>(p, acc, hi, row0, m0, shifted, y_rel, nl2, st, k2, cl2, grow);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (nb < 3) columns<nb + 1>(p, acc, wn, lane, hi, n0, tv, scale, row0, m0, shifted, k2, cl2);
   }
 };
 
