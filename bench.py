@@ -108,6 +108,9 @@ def main():
     ap.add_argument("--fp32-head-direct", action="store_true",
                     help="hand an fp32 head to the calls as fp32 (each call rounds and stages it, inside the "
                          "timed region) instead of rounding it once before timing")
+    ap.add_argument("--round-head-on-load", action="store_true",
+                    help="with --fp32-head-direct: the GEMMs round the fp32 head inside their tile loads "
+                         "(FLCE_FLAG_ROUND_HEAD_ON_LOAD: no staged copy, smaller workspace, slower)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -135,7 +138,7 @@ def main():
     T, H, V, Vu = w.T, w.H, w.V, w.Vu
     Tv = inp["n_valid"]
     p = L.make_problem(T, H, V, Vu, w.softcap, inp["ignore_index"], w.reduction, inp["num_label_tokens"],
-                       W.dtype)
+                       W.dtype, round_head_on_load=direct and args.round_head_on_load)
     ws = L.alloc_workspace(p, dev)
     loss = torch.empty((), dtype=torch.float32, device=dev)
     lse = torch.empty(T, dtype=torch.float32, device=dev)
@@ -304,7 +307,8 @@ def main():
         "config": {
             "workload": w.name,
             "tokens": T, "hidden": H, "vocab": V, "unpadded_vocab": Vu, "valid_tokens": Tv,
-            "softcap": w.softcap, "reduction": w.reduction, "head": str(W.dtype).replace("torch.", ""),
+            "softcap": w.softcap, "reduction": w.reduction, "head": str(W.dtype).replace("torch.", "")
+            + (" (rounded on load)" if direct and args.round_head_on_load else ""),
             "num_label_tokens": inp["num_label_tokens"],
             "credited_tflop_per_step": round(credited / 1e12, 3),
             "model_tflop_per_step": round(6.0 * Tv * Vu * H / 1e12, 3),

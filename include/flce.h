@@ -105,9 +105,22 @@ typedef enum flce_dtype {
  * weight_dtype      FLCE_DTYPE_BF16, or FLCE_DTYPE_FP32 for an fp32 head that
  *                   each call rounds to bf16 itself (Inkling2 page, class
  *                   description: an fp32 head is used at its bf16 value,
- *                   rounded to nearest even like torch's cast).  The rounded
- *                   copy of rows < Vu is staged in the workspace, which grows
- *                   by Vu*Hp*2 bytes; rows >= Vu are never read.
+ *                   rounded to nearest even like torch's cast).  By default
+ *                   each call stages the rounded copy of rows < Vu in the
+ *                   workspace (Vu*Hp*2 more bytes, one pass over the head per
+ *                   call); rows >= Vu are never read.
+ * flags             0, or FLCE_FLAG_ROUND_HEAD_ON_LOAD with an fp32 head whose
+ *                   H is a multiple of 128: no staged copy; the projection and
+ *                   recompute GEMMs read the fp32 head and round each piece on
+ *                   its way into their bf16 LDS tiles, and the recompute keeps
+ *                   one chunk's rounded rows for the dH contraction (vc*Hp*2
+ *                   workspace bytes instead of Vu*Hp*2).  Results equal the
+ *                   staged path's within rounding order (bit for bit where both
+ *                   use 256-row tiles).  It reads twice the head bytes per
+ *                   tile and runs slower (about 1.3x the staged step at
+ *                   T=8192, H=3072, Vu=256000): a choice of memory over time.
+ *                   Ignored for H not a multiple of 128 (the head is staged).
+ *                   Other bits are invalid.
  */
 typedef struct flce_problem {
   int64_t num_tokens;
@@ -119,7 +132,11 @@ typedef struct flce_problem {
   int64_t ignore_index;
   int64_t num_label_tokens;
   int32_t weight_dtype;
+  int32_t flags;
 } flce_problem_t;
+
+/* flce_problem_t.flags bits. */
+#define FLCE_FLAG_ROUND_HEAD_ON_LOAD 1
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* flce_status_string(int status);

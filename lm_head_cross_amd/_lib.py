@@ -21,6 +21,7 @@ FLCE_REDUCTION_SUM = 0
 FLCE_REDUCTION_MEAN = 1
 FLCE_DTYPE_BF16 = 0
 FLCE_DTYPE_FP32 = 1
+FLCE_FLAG_ROUND_HEAD_ON_LOAD = 1
 
 EXPORTED = ("flce_status_string", "flce_version", "flce_workspace_size", "flce_forward", "flce_forward_noalloc",
             "flce_backward",
@@ -44,6 +45,7 @@ class Problem(ctypes.Structure):
         ("ignore_index", ctypes.c_int64),
         ("num_label_tokens", ctypes.c_int64),
         ("weight_dtype", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
     ]
 
 

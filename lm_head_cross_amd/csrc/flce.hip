@@ -21,6 +21,7 @@
 
 #include "../../include/flce.h"
 #include "epilogues.hpp"
+#include "gemm_f32w.hpp"
 #include "gemm_wide.hpp"
 #include "host_common.hpp"
 
@@ -289,6 +290,8 @@ struct Plan {
   int64_t T, H, V, Vu;
   int64_t Hp;           // H rounded up to 128: the row length of Xc, XcT's row count and a staged head's rows
   bool stage_head;      // the kernels read a bf16 copy of the head's rows < Vu (fp32 head, or H != Hp)
+  bool f32_head;        // the GEMMs read an fp32 head directly, rounding each piece on its way into LDS
+                        // (FLCE_FLAG_ROUND_HEAD_ON_LOAD)
   int64_t Tvp;          // T rounded up to 256 (the token tile)
   int64_t tiles_t;      // Tvp / 256
   int64_t tiles_v;      // ceil(Vu / 256): forward vocab tiles
@@ -301,6 +304,7 @@ struct Plan {
   size_t off_wst;       // the staged head [Vu, Hp] bf16 (0 bytes when the caller's head is read directly)
   size_t off_part;      // forward region
   size_t off_g, off_hacc, off_xct;  // backward region
+  size_t off_wcopy;     // backward, fp32 head read directly: bf16 copy of one chunk's head rows [vc, Hp]
   size_t fwd_total;     // bytes the forward pass touches (a prefix of the workspace)
   size_t total;
 };
@@ -313,6 +317,8 @@ int validate(const flce_problem_t* p) {
   if (p->reduction != FLCE_REDUCTION_SUM && p->reduction != FLCE_REDUCTION_MEAN) return FLCE_ERR_INVALID_ARG;
   if (p->num_label_tokens == 0) return FLCE_ERR_INVALID_ARG;
   if (p->weight_dtype != FLCE_DTYPE_BF16 && p->weight_dtype != FLCE_DTYPE_FP32) return FLCE_ERR_UNSUPPORTED;
+  if ((p->flags & ~FLCE_FLAG_ROUND_HEAD_ON_LOAD) != 0) return FLCE_ERR_INVALID_ARG;
+  if ((p->flags & FLCE_FLAG_ROUND_HEAD_ON_LOAD) && p->weight_dtype != FLCE_DTYPE_FP32) return FLCE_ERR_INVALID_ARG;
   if (p->hidden % 8 != 0) return FLCE_ERR_UNSUPPORTED;
   // The GEMM loaders address a 256-row tile with 32-bit byte offsets from a
   // buffer resource of under 2 GB: 256 rows of ld bf16 elements must stay
@@ -397,7 +403,8 @@ Plan make_plan(const flce_problem_t* p, int n_cu = 256) {
   pl.V = p->vocab;
   pl.Vu = p->unpadded_vocab;
   pl.Hp = align_up((size_t)pl.H, 128);
-  pl.stage_head = p->weight_dtype == FLCE_DTYPE_FP32 || pl.Hp != pl.H;
+  pl.f32_head = p->weight_dtype == FLCE_DTYPE_FP32 && pl.Hp == pl.H && (p->flags & FLCE_FLAG_ROUND_HEAD_ON_LOAD);
+  pl.stage_head = (p->weight_dtype == FLCE_DTYPE_FP32 && !pl.f32_head) || pl.Hp != pl.H;
   pl.Tvp = align_up((size_t)pl.T, 256);
   pl.tiles_t = pl.Tvp / 256;
   pl.tiles_v = ceil_div(pl.Vu, 256);
@@ -421,8 +428,9 @@ Plan make_plan(const flce_problem_t* p, int n_cu = 256) {
   pl.off_scale = take(16);
   pl.off_bsum = take(pl.Tvp / kCombineTokens * 8);
   pl.off_xc = take(pl.Tvp * pl.Hp * 2);
-  // An fp32 head, or rows not a multiple of 128 long: the bf16 copy of its
-  // usable rows, staged here by each call.
+  // An fp32 head (unless rounded on load), or rows not a multiple of 128
+  // long: the bf16 copy of the head's usable rows, zero-padded to Hp and
+  // staged here by each call.
   pl.off_wst = take(pl.stage_head ? pl.Vu * pl.Hp * 2 : 0);
   const size_t common = o;
   pl.off_part = take(pl.tiles_v * pl.Tvp * 8);
@@ -432,6 +440,9 @@ Plan make_plan(const flce_problem_t* p, int n_cu = 256) {
   // Every chunk width below tiles_v gives more than one chunk.
   pl.off_hacc = take(pl.tiles_v > 1 ? pl.Tvp * pl.H * 4 : 0);
   pl.off_xct = take(pl.Tvp * pl.Hp * 2);
+  // An fp32 head read directly: the recompute writes the rounded rows of the
+  // chunk here for the chunk's dH contraction.
+  pl.off_wcopy = take(pl.f32_head ? ct_max * 256 * pl.Hp * 2 : 0);
   const size_t bwd_end = o;
   pl.fwd_total = fwd_end;
   pl.total = std::max(fwd_end, bwd_end);
@@ -463,16 +474,19 @@ void zero_fill(void* p, int64_t bytes, hipStream_t s) {
 
 // The bf16 head the kernels read, rows of Hp elements: the caller's for a
 // bf16 head with H a multiple of 128; otherwise its rows < Vu copied into
-// the workspace, an fp32 head rounded to nearest even ("nemo_automodel.
-// components.models.inkling2.loss", class description: an fp32 head is used
-// at its bf16 value), with zero columns H..Hp.
-// Rows >= Vu are never read.
+// the workspace with zero columns H..Hp, an fp32 head rounded to nearest
+// even ("nemo_automodel.components.models.inkling2.loss", class description:
+// an fp32 head is used at its bf16 value).  An fp32 head rounded on load
+// (FLCE_FLAG_ROUND_HEAD_ON_LOAD) is not staged: the projection and recompute
+// GEMMs read it directly (gemm_f32w.hpp), and this returns nullptr.  Rows
+// >= Vu are never read.
 const bf16* staged_head(const Plan& pl, const flce_problem_t& p, const void* weight, void* workspace,
                         hipStream_t stream) {
+  if (pl.f32_head) return nullptr;
   if (!pl.stage_head) return static_cast<const bf16*>(weight);
   bf16* wst = ws_at<bf16>(workspace, pl.off_wst);
   TraceScope tr(FLCE_KERNEL_AUX, 0.0, stream);
-  if (pl.Hp == pl.H) {
+  if (p.weight_dtype == FLCE_DTYPE_FP32 && pl.Hp == pl.H) {
     const int64_t n4 = pl.Vu * pl.H / 4;
     hipLaunchKernelGGL(k_round_bf16_vec, dim3(grid_for(n4, 256, 16384)), dim3(256), 0, stream,
                        static_cast<const float4*>(weight), reinterpret_cast<bf16x4*>(wst), n4);
@@ -625,17 +639,29 @@ int forward_impl(const flce_problem_t* problem, const void* hidden, const void* 
   const bf16* Wb = staged_head(pl, p, weight, workspace, stream);
   launch_compact_gather(pl, p, labels, hidden, meta, valid_idx, yc, device_status, lse, token_loss, xc, stream);
   // The projection runs with 384-row head tiles (gemm_wide.hpp) when the
-  // usable head has at least that many rows, else with 256-row tiles.
-  const bool wide = pl.Vu >= gemm::WBM;
+  // usable head has at least that many rows, else with 256-row tiles; an
+  // fp32 head read directly takes the 256-row tiles (gemm_f32w.hpp).
+  const bool wide = pl.Vu >= gemm::WBM && !pl.f32_head;
   const int64_t tiles_v = wide ? ceil_div(pl.Vu, gemm::WBM) : pl.tiles_v;
   {
     gemm::Operand A{Wb, pl.Hp, (int)pl.Vu - 1, 0};
+    gemm::OperandF32 Af{static_cast<const float*>(weight), pl.H, (int)pl.Vu - 1, 0};
     gemm::Operand B{xc, pl.Hp, (int)pl.Tvp - 1, 0};
     gemm::Schedule sch{(int)tiles_v, (int)pl.tiles_t, k_steps_for(pl.Hp), tv, 2};
     const dim3 grid(tiles_v * pl.tiles_t);
     const float c = p.softcap, inv_c = c > 0.0f ? 1.0f / c : 0.0f;
     TraceScope tr(FLCE_KERNEL_PROJ_LSE, 2.0 * pl.T * pl.Vu * pl.H, stream);
-    if (wide && c > 0.0f) {
+    if (pl.f32_head && c > 0.0f) {
+      using E = epi::Lse<true>;
+      E::Params ep{part, (int)pl.Tvp, label_logit, yc, tv, (int)pl.Vu, c, inv_c};
+      hipLaunchKernelGGL((gemm::gemm_kernel_f32a<E>), grid, dim3(gemm::NTHREADS), 0, stream, Af, B, sch, ep,
+                         (bf16*)nullptr);
+    } else if (pl.f32_head) {
+      using E = epi::Lse<false>;
+      E::Params ep{part, (int)pl.Tvp, label_logit, yc, tv, (int)pl.Vu, c, inv_c};
+      hipLaunchKernelGGL((gemm::gemm_kernel_f32a<E>), grid, dim3(gemm::NTHREADS), 0, stream, Af, B, sch, ep,
+                         (bf16*)nullptr);
+    } else if (wide && c > 0.0f) {
       using E = epi::Lse<true, gemm::WMB>;
       E::Params ep{part, (int)pl.Tvp, label_logit, yc, tv, (int)pl.Vu, c, inv_c};
       hipLaunchKernelGGL((gemm::gemm_wide_kernel<E>), grid, dim3(gemm::NTHREADS), 0, stream, A, B, sch, ep);
@@ -733,16 +759,36 @@ int flce_backward(const flce_problem_t* problem, const void* hidden, const void*
 
   const float inv_c = p.softcap > 0.0f ? 1.0f / p.softcap : 0.0f;
   const bool wide_h = dh_wide(pl.tiles_t, pl.tiles_h, pl.Tvp, pl.n_cu);
+  bf16* wcopy = ws_at<bf16>(workspace, pl.off_wcopy);
   for (int64_t c = 0; c < pl.nchunks; ++c) {
     const int64_t v0 = c * pl.vc;
     const int64_t vw = std::min(pl.vc, pl.Vu - v0);
     const int64_t tiles_c = ceil_div(vw, 256);
-    const bf16* Wc = W + v0 * pl.Hp;
+    // The chunk's bf16 head rows: the caller's or staged head, or (an fp32
+    // head read directly) the copy the chunk's recompute writes.
+    const bf16* Wc = pl.f32_head ? wcopy : W + v0 * pl.Hp;
+    const float* Wcf = static_cast<const float*>(weight) + v0 * pl.H;
     const double chunk_flops = 2.0 * pl.T * vw * pl.H;
 
     // 1. logits of the chunk -> G (bf16, token-major); 384-row tiles when
-    //    the chunk has at least 384 rows.
-    {
+    //    the chunk has at least 384 rows (256-row tiles for an fp32 head
+    //    read directly).
+    if (pl.f32_head) {
+      gemm::OperandF32 A{Wcf, pl.H, (int)vw - 1, 0};
+      gemm::Operand B{xc, pl.Hp, (int)pl.Tvp - 1, 0};
+      gemm::Schedule sch{(int)tiles_c, (int)pl.tiles_t, k_steps_for(pl.Hp), tv, 2};
+      const dim3 grid(tiles_c * pl.tiles_t);
+      TraceScope tr(FLCE_KERNEL_RECOMPUTE_G, chunk_flops, stream);
+      if (p.softcap > 0.0f) {
+        using E = epi::Grad<true>;
+        E::Params ep{G, pl.vc, (int)v0, (int)vw, lse, valid_idx, yc, tv, scale, p.softcap, inv_c};
+        hipLaunchKernelGGL((gemm::gemm_kernel_f32a<E>), grid, dim3(gemm::NTHREADS), 0, stream, A, B, sch, ep, wcopy);
+      } else {
+        using E = epi::Grad<false>;
+        E::Params ep{G, pl.vc, (int)v0, (int)vw, lse, valid_idx, yc, tv, scale, 0.0f, 0.0f};
+        hipLaunchKernelGGL((gemm::gemm_kernel_f32a<E>), grid, dim3(gemm::NTHREADS), 0, stream, A, B, sch, ep, wcopy);
+      }
+    } else {
       const bool wide = vw >= gemm::WBM;
       const int64_t tiles_r = wide ? ceil_div(vw, gemm::WBM) : tiles_c;
       gemm::Operand A{Wc, pl.Hp, (int)vw - 1, 0};

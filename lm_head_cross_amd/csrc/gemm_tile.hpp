@@ -436,32 +436,39 @@ __device__ __forceinline__ int acc_row(int wm, int mb, int r, int lane) {
 }
 __device__ __forceinline__ int acc_col(int wn, int nb, int lane) { return wn * 128 + 32 * nb + (lane & 31); }
 
-// One tile: schedule, early exit for tiles past the valid tokens, main loop,
-// then the epilogue (which may reuse the first stage's LDS).
-template <bool A_KMAJOR, bool B_KMAJOR, class Epi>
-__device__ __forceinline__ void run_tile(const Operand& A, const Operand& B, const Schedule& sch,
-                                         const typename Epi::Params& ep, int pid, bf16* s0, bf16* s1, bf16* s2,
-                                         bf16* s3) {
-  // With tokens along M or N, the grid covers every token tile the host
-  // allows for, but only ceil(Tv / 256) of them hold valid tokens (Tv is
-  // read on the device).  The workgroup ids are mapped onto those tiles
-  // alone and the rest exit: mapped over the full grid, the tiles past Tv
-  // took whole XCDs' shares (tile_of gives each XCD a contiguous run), and
-  // at half the tokens ignored half the XCDs sat idle in dH.
+// Workgroup pid's tile: its first rows (m0, n0) and K steps; false for a
+// workgroup with no tile.  With tokens along M or N, the grid covers every
+// token tile the host allows for, but only ceil(Tv / 256) of them hold valid
+// tokens (Tv is read on the device).  The workgroup ids are mapped onto those
+// tiles alone and the rest exit: mapped over the full grid, the tiles past Tv
+// took whole XCDs' shares (tile_of gives each XCD a contiguous run), and at
+// half the tokens ignored half the XCDs sat idle in dH.
+__device__ __forceinline__ bool map_tile(const Schedule& sch, int pid, int& m0, int& n0, int& k_steps) {
   int tiles_m = sch.tiles_m, tiles_n = sch.tiles_n;
-  int k_steps = sch.k_steps;
+  k_steps = sch.k_steps;
   if (sch.tok_dim != 0) {
     const int tv = *sch.tok_count;
     const int tok_tiles = (tv + BM - 1) / BM;
     if (sch.tok_dim == 1) tiles_m = min(tiles_m, tok_tiles);
     if (sch.tok_dim == 2) tiles_n = min(tiles_n, tok_tiles);
     if (sch.tok_dim == 3) k_steps = (tv + NST * BK - 1) / (NST * BK) * NST;
-    if (pid >= tiles_m * tiles_n) return;
+    if (pid >= tiles_m * tiles_n) return false;
   }
   int tm, tn;
   tile_of(pid, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM;
-  const int n0 = tn * BN;
+  m0 = tm * BM;
+  n0 = tn * BN;
+  return true;
+}
+
+// One tile: schedule, early exit for tiles past the valid tokens, main loop,
+// then the epilogue (which may reuse the first stage's LDS).
+template <bool A_KMAJOR, bool B_KMAJOR, class Epi>
+__device__ __forceinline__ void run_tile(const Operand& A, const Operand& B, const Schedule& sch,
+                                         const typename Epi::Params& ep, int pid, bf16* s0, bf16* s1, bf16* s2,
+                                         bf16* s3) {
+  int m0, n0, k_steps;
+  if (!map_tile(sch, pid, m0, n0, k_steps)) return;
   f32x16 acc[4][4];
   if constexpr (A_KMAJOR && B_KMAJOR) mainloop_kk(A, B, m0, n0, k_steps, s0, s1, s2, s3, acc);
   else mainloop_mn<A_KMAJOR, B_KMAJOR>(A, B, m0, n0, k_steps, s0, s1, s2, s3, acc);

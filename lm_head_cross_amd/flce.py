@@ -41,10 +41,13 @@ _WEIGHT_DTYPES = {torch.bfloat16: _lib.FLCE_DTYPE_BF16, torch.float32: _lib.FLCE
 
 def make_problem(num_tokens: int, hidden: int, vocab: int, unpadded_vocab: int | None = None,
                  softcap: float = 0.0, ignore_index: int = -100, reduction: str = "sum",
-                 num_label_tokens: int | None = None, weight_dtype=torch.bfloat16) -> _lib.Problem:
+                 num_label_tokens: int | None = None, weight_dtype=torch.bfloat16,
+                 round_head_on_load: bool = False) -> _lib.Problem:
     """Fill an ``flce_problem_t``; value checks are the library's.  With
     ``weight_dtype=torch.float32`` the calls take the fp32 head and round its
-    usable rows to bf16 themselves."""
+    usable rows to bf16 themselves: staged in the workspace, or with
+    ``round_head_on_load`` inside the GEMMs' tile loads (smaller workspace,
+    slower; see include/flce.h)."""
     if weight_dtype not in _WEIGHT_DTYPES:
         raise NotImplementedError(f"the head must be bfloat16 or float32, got {weight_dtype}")
     if reduction not in _REDUCTIONS:
@@ -56,7 +59,8 @@ def make_problem(num_tokens: int, hidden: int, vocab: int, unpadded_vocab: int |
         unpadded_vocab=int(vocab if unpadded_vocab is None else unpadded_vocab),
         softcap=float(softcap), reduction=_REDUCTIONS[reduction], ignore_index=int(ignore_index),
         num_label_tokens=-1 if num_label_tokens is None else int(num_label_tokens),
-        weight_dtype=_WEIGHT_DTYPES[weight_dtype])
+        weight_dtype=_WEIGHT_DTYPES[weight_dtype],
+        flags=_lib.FLCE_FLAG_ROUND_HEAD_ON_LOAD if round_head_on_load else 0)
 
 
 def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:

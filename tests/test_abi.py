@@ -73,12 +73,22 @@ def test_workspace_size_bounds():
         assert code == _lib.FLCE_OK and w < T * V * 2
 
 
-def test_fp32_head_workspace_holds_the_staged_rows():
+def test_fp32_head_workspace():
+    """An fp32 head is staged by default (the workspace holds a bf16 copy of
+    the usable rows); rounded on load it needs no staged copy, only one
+    backward chunk's rounded rows.  With H not a multiple of 128 the head is
+    staged either way."""
     import torch
     a = _ws(make_problem(8192, 3072, 262144, 256000, softcap=30.0))
     b = _ws(make_problem(8192, 3072, 262144, 256000, softcap=30.0, weight_dtype=torch.float32))
-    assert a[0] == b[0] == _lib.FLCE_OK
+    c = _ws(make_problem(8192, 3072, 262144, 256000, softcap=30.0, weight_dtype=torch.float32,
+                         round_head_on_load=True))
+    assert a[0] == b[0] == c[0] == _lib.FLCE_OK
     assert b[1] - a[1] == 256000 * 3072 * 2  # bf16 copy of the usable rows only
+    assert a[1] < c[1] <= a[1] + 256000 * 3072 * 2 // 4  # at most a quarter of the usable rows
+    d = _ws(make_problem(4096, 2880, 201088, 200000, weight_dtype=torch.float32))
+    e = _ws(make_problem(4096, 2880, 201088, 200000, weight_dtype=torch.float32, round_head_on_load=True))
+    assert d[0] == e[0] == _lib.FLCE_OK and d[1] == e[1]
 
 
 def test_unaligned_hidden_stages_a_padded_head():
@@ -125,6 +135,8 @@ def test_library_source_allocates_no_device_memory():
     (dict(hidden=12), _lib.FLCE_ERR_UNSUPPORTED),
     (dict(hidden=4100), _lib.FLCE_ERR_UNSUPPORTED),
     (dict(weight_dtype=7), _lib.FLCE_ERR_UNSUPPORTED),
+    (dict(flags=2), _lib.FLCE_ERR_INVALID_ARG),
+    (dict(flags=1), _lib.FLCE_ERR_INVALID_ARG),  # rounding on load needs an fp32 head
     # 32-bit tile offsets: beyond these sizes the call is refused
     (dict(num_tokens=(1 << 21) + 1), _lib.FLCE_ERR_UNSUPPORTED),
     (dict(vocab=(1 << 23) + 8, unpadded_vocab=1000), _lib.FLCE_ERR_UNSUPPORTED),

@@ -68,24 +68,69 @@ def test_small_full_parity(name):
 
 
 def test_fp32_head_handed_over_directly():
-    """An fp32 head passed to the calls as fp32 (the library rounds and stages
-    its usable rows) gives the oracle's result and exactly the bf16-head
-    path's, bit for bit; padding rows are never read."""
+    """An fp32 head passed to the calls as fp32.  Staged (the default: each
+    call rounds the usable rows into the workspace): bit for bit the
+    pre-rounded bf16 head's results.  Rounded on load (inside the GEMMs'
+    tile loads): the oracle's result, and the pre-rounded head's within the
+    tolerances (it takes 256-row tiles where the bf16 head takes 384-row
+    ones, so the per-tile lse partials round differently).  Padding rows are
+    never read in either mode (NaN there changes nothing, bit for bit)."""
     w = SMALL["fp32_head"]
     inp = make_inputs(w, argmax_device="cuda:0")
-    a = run_hip(inp, fp32_head_direct=True)
-    check_full(inp, a, label="fp32 head direct")
     b = run_hip(inp)
+    a = run_hip(inp, fp32_head_direct=True)
+    check_full(inp, a, label="fp32 head staged")
     assert a["loss"] == b["loss"]
     for k in ("lse", "token_loss", "dX", "dW"):
         assert torch.equal(a[k], b[k]), k
+    r = run_hip(inp, fp32_head_direct=True, round_on_load=True)
+    check_full(inp, r, label="fp32 head rounded on load")
+    assert abs(r["loss"] - b["loss"]) <= TOL_TOTAL_REL * abs(b["loss"])
+    assert (r["token_loss"] - b["token_loss"]).abs().max().item() <= TOL_TOKEN_ABS
+    for k in ("dX", "dW"):
+        assert rel_l2(r[k].double().numpy(), b[k].double().numpy()) <= TOL_GRAD_REL_L2, k
     poisoned = dict(inp)
     W = inp["weight"].clone()
     W[w.Vu:] = float("nan")
     poisoned["weight"] = W
-    c = run_hip(poisoned, fp32_head_direct=True)
+    for ref, rol in ((a, False), (r, True)):
+        c = run_hip(poisoned, fp32_head_direct=True, round_on_load=rol)
+        for k in ("lse", "token_loss", "dX", "dW"):
+            assert torch.equal(ref[k], c[k]), (k, rol)
+
+
+def _tie_head(w, seed):
+    """An fp32 head whose every element is an exact tie between two bf16
+    values (low 16 bits 0x8000), half with an even and half with an odd kept
+    bit, plus some values that round up or down: round to nearest even is
+    the only rounding that gives the pre-rounded head's values."""
+    g = torch.Generator().manual_seed(seed)
+    base = (torch.randn(w.V, w.H, generator=g) * w.w_std).to(torch.bfloat16).to(torch.float32)
+    bits = base.view(torch.int32)
+    tie = bits | 0x8000
+    low = torch.randint(1, 0x10000, (w.V, w.H), generator=g, dtype=torch.int32)
+    pick = torch.rand(w.V, w.H, generator=g) < 0.8
+    return torch.where(pick, tie, bits | low).view(torch.float32)
+
+
+@pytest.mark.parametrize("softcap", [0.0, 30.0])
+def test_fp32_head_rounding_on_load_is_the_bf16_cast(softcap):
+    """With fewer than 384 usable rows and at most 256 tokens both paths run
+    the same 256-row tiles, so the fp32 head rounded on its way into LDS
+    (FLCE_FLAG_ROUND_HEAD_ON_LOAD) must
+    give, bit for bit, the results of the head rounded beforehand by
+    flce_round_to_bf16 (torch's cast, checked against the oracle's rounding
+    below): every head element is a rounding tie or near one."""
+    w = _small(120, T=250, H=256, V=383, Vu=350, w_std=0.3, ignore_frac=0.05, softcap=softcap)
+    inp = dict(make_inputs(w))
+    inp["weight"] = _tie_head(w, 5)
+    a = run_hip(inp, fp32_head_direct=True, round_on_load=True)
+    b = run_hip(inp)
+    assert a["status"] == b["status"] == 0
+    assert a["loss"] == b["loss"]
     for k in ("lse", "token_loss", "dX", "dW"):
-        assert torch.equal(a[k], c[k]), k
+        assert torch.equal(a[k], b[k]), k
+    check_full(inp, a, label=f"fp32 tie head, c={softcap}")
 
 
 def test_grad_out_scaling():
@@ -265,10 +310,11 @@ def test_round_to_bf16_matches_oracle_rounding():
 # ---------------------------------------------------------------------------
 
 
-def test_workload3_fp32_head_direct_matches_staged_cast():
+def test_workload3_fp32_head_direct_staged_matches_pre_rounded():
     """Softcapped padded head (fp32 head, V=262144, Vu=256000) at full size:
-    handing the fp32 head over directly is bit-identical to rounding it first
-    (the rounded path is checked against the oracle below)."""
+    handing the fp32 head over directly (staged by each call) is
+    bit-identical to rounding it first (the rounded path, and the head
+    rounded on load, are checked against the oracle below)."""
     w = WORKLOADS[3]
     inp = make_inputs(w)
     rows = np.arange(0, w.T, 97)
@@ -280,14 +326,17 @@ def test_workload3_fp32_head_direct_matches_staged_cast():
         assert torch.equal(a[k], b[k]), k
 
 
-@pytest.mark.parametrize("key", [2, 3, 4, 5])
-def test_workload_full_size(key):
+@pytest.mark.parametrize("key,on_load", [(2, False), (3, False), (3, True), (4, False), (5, False)])
+def test_workload_full_size(key, on_load):
+    """Full-size workloads; workload 3's fp32 head also handed over directly
+    and rounded to bf16 inside the GEMMs' tile loads."""
     w = WORKLOADS[key]
-    say(f"workload {key}: {w.name}")
+    say(f"workload {key}: {w.name}" + (" (fp32 head rounded on load)" if on_load else ""))
     inp = make_inputs(w, argmax_device="cuda:0")
     y = inp["labels"].numpy()
     tok, voc = sample_rows(w, y)
-    res = run_hip(inp, dx_rows=tok, dw_rows=voc, keep_device=True)
+    res = run_hip(inp, dx_rows=tok, dw_rows=voc, keep_device=True, fp32_head_direct=on_load,
+                  round_on_load=on_load)
     assert res["status"] == 0
     if w.V > w.Vu:
         assert res["dW_dev"][w.Vu:].abs().max().item() == 0.0
