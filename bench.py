@@ -53,9 +53,24 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, n_tokens):
     """Time the oracle (fwd + bwd, full vocabulary) on the first n_tokens
-    positions of the workload; returns tokens/s and what was run."""
+    positions of the workload; returns tokens/s, what was run, the CPU, and
+    the whole workload's time extrapolated from the sample (the oracle's work
+    is linear in the positions: each one's logits, softmax and gradient rows,
+    and its share of dW)."""
     import numpy as np
 
     import oracle
@@ -75,6 +90,7 @@ def cpu_baseline(inp, n_tokens):
     oracle.forward(X, W, y, p, row_block=256)
     oracle.backward(X, W, y, p, row_block=256)
     dt = time.perf_counter() - t0
+    T = inp["hidden"].shape[0]
     return {
         "value": n_tokens / dt,
         "unit": "tokens/s",
@@ -82,6 +98,9 @@ def cpu_baseline(inp, n_tokens):
         "kind": "oracle",
         "sample": f"first {n_tokens} positions of the workload, fwd+bwd over the full vocabulary "
                   f"(fp64 numpy, {dt:.1f} s)",
+        "cpu_model": cpu_model(),
+        "logical_cpus": os.cpu_count(),
+        "extrapolated_full_workload_s": round(dt * T / n_tokens, 1),
     }
 
 
@@ -251,7 +270,8 @@ def main():
     tokens_per_s = T / (ms * 1e-3)
     pct_peak = credited / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12) * 100.0
     log(f"step {ms:.3f} ms  {tokens_per_s:,.0f} tokens/s  {pct_peak:.1f}% of bf16 peak "
-        f"(credited {credited / 1e12:.2f} TFLOP)  loss={loss.item():.6g}")
+        f"(credited {credited / 1e12:.2f} TFLOP; {pct_peak * 0.75:.1f}% on the 6 Tv Vu H model flops)  "
+        f"loss={loss.item():.6g}")
     log(f"  per step: median {med(step_ms):.3f} ms, min {step_ms[0]:.3f} ms; forward {med(fwd_ms):.3f} ms, "
         f"backward {med(bwd_ms):.3f} ms (medians); {n_cu} CUs -> peak {peak_dev:.1f} TFLOP/s")
     log(f"  without the launch trace: {untraced_ms:.3f} ms per step")
@@ -304,6 +324,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "pct_of_bf16_peak": round(pct_peak, 2),
+        "pct_of_bf16_peak_model_flops": round(pct_peak * 6.0 / 8.0, 2),
         "config": {
             "workload": w.name,
             "tokens": T, "hidden": H, "vocab": V, "unpadded_vocab": Vu, "valid_tokens": Tv,
@@ -349,9 +370,12 @@ def cpu_baseline_ce(inp, n_rows):
     oracle.ce_forward(z, y, p, mask=m)
     oracle.ce_backward(z, y, p, mask=m)
     dt = time.perf_counter() - t0
+    T = inp["logits"].shape[0]
     return {"value": n_rows / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {n_rows} positions of the workload, fwd+bwd over the full vocabulary "
-                      f"(fp64 numpy, {dt:.1f} s)"}
+                      f"(fp64 numpy, {dt:.1f} s)",
+            "cpu_model": cpu_model(), "logical_cpus": os.cpu_count(),
+            "extrapolated_full_workload_s": round(dt * T / n_rows, 1)}
 
 
 def bench_chunked_ce(args):
