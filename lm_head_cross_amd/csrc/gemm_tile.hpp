@@ -350,8 +350,13 @@ __device__ __forceinline__ void mainloop_kk(const Operand& A, const Operand& B, 
     stage_kk<true, true>(s0, s1, s2, s3, D, la, lb, wave, wm, wn, lane, fa, fb, acc);
     stage_kk<true, true>(s2, s3, s0, s1, D + 1, la, lb, wave, wm, wn, lane, fa, fb, acc);
   }
-  stage_kk<true, false>(s0, s1, s2, s3, D, la, lb, wave, wm, wn, lane, fa, fb, acc);
-  stage_kk<false, false>(s2, s3, s0, s1, D + 1, la, lb, wave, wm, wn, lane, fa, fb, acc);
+  // The two stages after the loop take the lane index through an opaque
+  // move, so that their LDS addresses are computed here rather than before
+  // the loop and kept in scratch across it.
+  int lane_t = lane;
+  asm volatile("" : "+v"(lane_t));
+  stage_kk<true, false>(s0, s1, s2, s3, D, la, lb, wave, wm, wn, lane_t, fa, fb, acc);
+  stage_kk<false, false>(s2, s3, s0, s1, D + 1, la, lb, wave, wm, wn, lane_t, fa, fb, acc);
   stage_barrier<0>();
 }
 
@@ -425,8 +430,10 @@ __device__ __forceinline__ void mainloop_mn(const Operand& A, const Operand& B, 
     stage_mn<A_KMAJOR, B_KMAJOR, true, true>(s0, s1, s2, s3, D, la, lb, wave, wm, wn, lane, fa, fb, acc);
     stage_mn<A_KMAJOR, B_KMAJOR, true, true>(s2, s3, s0, s1, D + 1, la, lb, wave, wm, wn, lane, fa, fb, acc);
   }
-  stage_mn<A_KMAJOR, B_KMAJOR, true, false>(s0, s1, s2, s3, D, la, lb, wave, wm, wn, lane, fa, fb, acc);
-  stage_mn<A_KMAJOR, B_KMAJOR, false, false>(s2, s3, s0, s1, D + 1, la, lb, wave, wm, wn, lane, fa, fb, acc);
+  int lane_t = lane;  // as in mainloop_kk
+  asm volatile("" : "+v"(lane_t));
+  stage_mn<A_KMAJOR, B_KMAJOR, true, false>(s0, s1, s2, s3, D, la, lb, wave, wm, wn, lane_t, fa, fb, acc);
+  stage_mn<A_KMAJOR, B_KMAJOR, false, false>(s2, s3, s0, s1, D + 1, la, lb, wave, wm, wn, lane_t, fa, fb, acc);
   stage_barrier<0>();
 }
 

@@ -186,8 +186,13 @@ __device__ __forceinline__ void mainloop_w(const Operand& A, const Operand& B, i
     stage_w<true, true>(s0, s1, s2, s3, D, la, lb, wave, wm, wn, lane, fa, fb, acc);
     stage_w<true, true>(s2, s3, s0, s1, D + 1, la, lb, wave, wm, wn, lane, fa, fb, acc);
   }
-  stage_w<true, false>(s0, s1, s2, s3, D, la, lb, wave, wm, wn, lane, fa, fb, acc);
-  stage_w<false, false>(s2, s3, s0, s1, D + 1, la, lb, wave, wm, wn, lane, fa, fb, acc);
+  // The two stages after the loop take the lane index through an opaque
+  // move, so that their LDS addresses are computed here rather than before
+  // the loop and kept in scratch across it.
+  int lane_t = lane;
+  asm volatile("" : "+v"(lane_t));
+  stage_w<true, false>(s0, s1, s2, s3, D, la, lb, wave, wm, wn, lane_t, fa, fb, acc);
+  stage_w<false, false>(s2, s3, s0, s1, D + 1, la, lb, wave, wm, wn, lane_t, fa, fb, acc);
   stage_barrier<0>();
   acc_fence(acc);
 }
@@ -329,8 +334,10 @@ __device__ __forceinline__ void mainloop_kmn(const Operand& A, const Operand& B,
     stage_kmn<true, true>(s0, s1, s2, s3, D, la, lb, wave, wm, wn, lane, fa, fb, acc);
     stage_kmn<true, true>(s2, s3, s0, s1, D + 1, la, lb, wave, wm, wn, lane, fa, fb, acc);
   }
-  stage_kmn<true, false>(s0, s1, s2, s3, D, la, lb, wave, wm, wn, lane, fa, fb, acc);
-  stage_kmn<false, false>(s2, s3, s0, s1, D + 1, la, lb, wave, wm, wn, lane, fa, fb, acc);
+  int lane_t = lane;  // as in mainloop_w
+  asm volatile("" : "+v"(lane_t));
+  stage_kmn<true, false>(s0, s1, s2, s3, D, la, lb, wave, wm, wn, lane_t, fa, fb, acc);
+  stage_kmn<false, false>(s2, s3, s0, s1, D + 1, la, lb, wave, wm, wn, lane_t, fa, fb, acc);
   stage_barrier<0>();
   acc_fence(acc);
 }
