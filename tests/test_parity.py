@@ -401,3 +401,30 @@ def test_no_logits_sized_allocation():
         f"bf16 [T, Vu] {w.T * w.Vu * 2 / 2**20:.1f} MiB")
     assert extra < w.T * w.Vu * 2
     assert math.isfinite(loss.item())
+
+
+@pytest.mark.parametrize("softcap", [0.0, 30.0])
+def test_single_usable_row(softcap):
+    """Vu = 1 (the degenerate softmax over one row): every valid token's loss,
+    and both gradients, are exactly 0 mathematically (softmax = one-hot).  In
+    fp32 the kernels reach them up to rounding: |loss_t| and every gradient
+    element stay below 1e-5 of their natural scales, padding rows of dW are
+    exactly 0 and the oracle gives exact zeros."""
+    w = _small(121, T=300, H=128, V=8, Vu=1, w_std=0.5, pad_std=10.0, softcap=softcap, ignore_frac=0.1)
+    inp = dict(make_inputs(w))
+    y = inp["labels"].clone()
+    y[y != -100] = 0
+    inp["labels"] = y
+    X, W = oracle.to_f64(inp["hidden"]), oracle.head_values(inp["weight"])
+    ref = oracle.forward(X, W, y.numpy(), oracle_problem(inp))
+    rdX, rdW = oracle.backward(X, W, y.numpy(), oracle_problem(inp))
+    assert ref.loss == 0.0 and not rdX.any() and not rdW.any()
+    res = run_hip(inp)
+    assert res["status"] == 0
+    assert res["token_loss"].abs().max().item() <= 1e-5
+    assert abs(res["loss"]) <= 1e-5 * ref.n_valid
+    wmax = inp["weight"][:1].float().abs().max().item()
+    xmax = inp["hidden"].float().abs().max().item()
+    assert res["dX"].float().abs().max().item() <= 1e-5 * wmax
+    assert res["dW"][:1].abs().max().item() <= 1e-5 * xmax * ref.n_valid
+    assert torch.all(res["dW"][1:] == 0)

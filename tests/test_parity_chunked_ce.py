@@ -292,3 +292,24 @@ def test_workload_full_size(key):
     assert e <= TOL_GRAD_REL_L2
     check_rows(res["dz_rows"][torch.from_numpy(sel)].double().numpy(), g_ref, "d_logits")
     assert torch.all(res["dz_rows"][torch.from_numpy(~sel)] == 0)
+
+
+def test_one_class():
+    """V = 1: the softmax over one class is 1, so every counted position's
+    loss and gradient are exactly 0; the kernels reach them up to rounding."""
+    g = torch.Generator().manual_seed(3)
+    for dtype in (torch.bfloat16, torch.float32):
+        z = (torch.randn(300, 1, generator=g) * 5).to(dtype)
+        y = torch.zeros(300, dtype=torch.int64)
+        y[::7] = -100
+        inp = {"logits": z, "labels": y, "mask": None, "ignore_index": -100, "reduction": "sum",
+               "num_label_tokens": None}
+        ref = oracle.ce_forward(oracle.to_f64(z), y.numpy(), _ref_problem(inp))
+        assert ref.loss == 0.0
+        res = _run(inp)
+        assert res["status"] == 0
+        assert res["token_loss"].abs().max().item() <= 1e-5
+        assert res["dz"].abs().max().item() <= 1e-6
+        counted = y != -100
+        zc = z[counted, 0].float()
+        assert torch.all((res["lse"][counted] - zc).abs() <= 1e-6 * (1 + zc.abs()))
