@@ -130,6 +130,9 @@ def main():
     ap.add_argument("--round-head-on-load", action="store_true",
                     help="with --fp32-head-direct: the GEMMs round the fp32 head inside their tile loads "
                          "(FLCE_FLAG_ROUND_HEAD_ON_LOAD: no staged copy, smaller workspace, slower)")
+    ap.add_argument("--dw-tile", type=int, choices=(256, 384), default=None,
+                    help="fix the tile of the backward's dW contraction (FLCE_FLAG_DW_TILE_256 / _384); by "
+                         "default the library picks it")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -157,7 +160,7 @@ def main():
     T, H, V, Vu = w.T, w.H, w.V, w.Vu
     Tv = inp["n_valid"]
     p = L.make_problem(T, H, V, Vu, w.softcap, inp["ignore_index"], w.reduction, inp["num_label_tokens"],
-                       W.dtype, round_head_on_load=direct and args.round_head_on_load)
+                       W.dtype, round_head_on_load=direct and args.round_head_on_load, dw_tile=args.dw_tile)
     ws = L.alloc_workspace(p, dev)
     loss = torch.empty((), dtype=torch.float32, device=dev)
     lse = torch.empty(T, dtype=torch.float32, device=dev)
@@ -331,6 +334,7 @@ def main():
             "softcap": w.softcap, "reduction": w.reduction, "head": str(W.dtype).replace("torch.", "")
             + (" (rounded on load)" if direct and args.round_head_on_load else ""),
             "num_label_tokens": inp["num_label_tokens"],
+            "dw_tile": args.dw_tile or "library's choice",
             "credited_tflop_per_step": round(credited / 1e12, 3),
             "model_tflop_per_step": round(6.0 * Tv * Vu * H / 1e12, 3),
             "label_tokens_per_s": round(Tv / (ms * 1e-3), 1),

@@ -120,7 +120,14 @@ typedef enum flce_dtype {
  *                   tile and runs slower (about 1.3x the staged step at
  *                   T=8192, H=3072, Vu=256000): a choice of memory over time.
  *                   Ignored for H not a multiple of 128 (the head is staged).
- *                   Other bits are invalid.
+ *                   FLCE_FLAG_DW_TILE_256 or FLCE_FLAG_DW_TILE_384 (at most
+ *                   one; 384 needs H >= 384) fix the tile of the backward's
+ *                   dW contraction, which the library otherwise picks with
+ *                   the vocabulary chunk width from an estimate of rounds of
+ *                   tiles on the device's compute units: 256-row tiles of
+ *                   G^T Xc, or 384-row tiles of Xc^T G stored transposed.
+ *                   Either gives the same result up to the order of fp32
+ *                   rounding.  Other bits are invalid.
  */
 typedef struct flce_problem {
   int64_t num_tokens;
@@ -137,6 +144,8 @@ typedef struct flce_problem {
 
 /* flce_problem_t.flags bits. */
 #define FLCE_FLAG_ROUND_HEAD_ON_LOAD 1
+#define FLCE_FLAG_DW_TILE_256 2
+#define FLCE_FLAG_DW_TILE_384 4
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* flce_status_string(int status);

@@ -22,6 +22,8 @@ FLCE_REDUCTION_MEAN = 1
 FLCE_DTYPE_BF16 = 0
 FLCE_DTYPE_FP32 = 1
 FLCE_FLAG_ROUND_HEAD_ON_LOAD = 1
+FLCE_FLAG_DW_TILE_256 = 2
+FLCE_FLAG_DW_TILE_384 = 4
 
 EXPORTED = ("flce_status_string", "flce_version", "flce_workspace_size", "flce_forward", "flce_forward_noalloc",
             "flce_backward",

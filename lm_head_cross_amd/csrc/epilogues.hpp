@@ -293,6 +293,49 @@ struct StoreF32 {
   }
 };
 
+// A transposed fp32 tile: accumulator rows are hidden columns h, accumulator
+// columns are rows v of the output, stored at out[v * ldo + h] (dW computed
+// as Xc^T G).  A lane's registers 4q..4q+3 of a block are 4 consecutive h of
+// one v: one 16-byte store each.  H is a multiple of 8 and a0 / m0 are too,
+// so each such group lies wholly inside or outside [m0, hcols).  Rows below
+// m0 (a last tile computed shifted down) belong to the tile before.  Plain
+// stores: the 32-byte pieces of 4 consecutive stores fill whole 128-byte
+// lines, which the L2 merges before they go out.
+template <int MB>
+struct StoreF32T {
+  struct Params {
+    float* out;
+    int64_t ldo;
+    int vrows;   // columns v >= vrows are not stored
+    int hcols;   // accumulator rows h >= hcols are not stored
+  };
+  static constexpr int kWaveRows = 32 * MB;
+
+  static __device__ __forceinline__ void apply(const Params& p, f32x16 (&acc)[MB][4], int m0, int a0, int n0,
+                                               bf16*) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int v = n0 + acc_col(wn, nb, lane);
+      if (v >= p.vrows) continue;
+      float* row = p.out + (int64_t)v * p.ldo;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int h = a0 + wm * kWaveRows + 32 * mb + 8 * q + 4 * (lane >> 5);
+          if (h < m0 || h >= p.hcols) continue;
+          const float4 x = make_float4(acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1], acc[mb][nb][4 * q + 2],
+                                       acc[mb][nb][4 * q + 3]);
+          *reinterpret_cast<float4*>(row + h) = x;
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+};
+
 // dHidden: fp32 accumulation over the vocabulary chunks in a fixed order; the
 // last chunk rounds to bf16 and writes each compacted token's row back to its
 // original position.

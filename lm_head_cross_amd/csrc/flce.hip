@@ -298,6 +298,7 @@ struct Plan {
   int64_t tiles_h;      // ceil(H / 256)
   int64_t vc;           // backward vocabulary chunk width (multiple of 256)
   int64_t nchunks;
+  bool dw_wide;         // dW of a chunk as 384-row tiles of Xc^T G (stored transposed)
   int n_cu;             // compute units the chunk width was chosen for
   // workspace byte offsets
   size_t off_meta, off_valid, off_yc, off_label, off_scale, off_bsum, off_xc;
@@ -317,7 +318,10 @@ int validate(const flce_problem_t* p) {
   if (p->reduction != FLCE_REDUCTION_SUM && p->reduction != FLCE_REDUCTION_MEAN) return FLCE_ERR_INVALID_ARG;
   if (p->num_label_tokens == 0) return FLCE_ERR_INVALID_ARG;
   if (p->weight_dtype != FLCE_DTYPE_BF16 && p->weight_dtype != FLCE_DTYPE_FP32) return FLCE_ERR_UNSUPPORTED;
-  if ((p->flags & ~FLCE_FLAG_ROUND_HEAD_ON_LOAD) != 0) return FLCE_ERR_INVALID_ARG;
+  if ((p->flags & ~(FLCE_FLAG_ROUND_HEAD_ON_LOAD | FLCE_FLAG_DW_TILE_256 | FLCE_FLAG_DW_TILE_384)) != 0)
+    return FLCE_ERR_INVALID_ARG;
+  if ((p->flags & FLCE_FLAG_DW_TILE_256) && (p->flags & FLCE_FLAG_DW_TILE_384)) return FLCE_ERR_INVALID_ARG;
+  if ((p->flags & FLCE_FLAG_DW_TILE_384) && p->hidden < 384) return FLCE_ERR_INVALID_ARG;
   if ((p->flags & FLCE_FLAG_ROUND_HEAD_ON_LOAD) && p->weight_dtype != FLCE_DTYPE_FP32) return FLCE_ERR_INVALID_ARG;
   if (p->hidden % 8 != 0) return FLCE_ERR_UNSUPPORTED;
   // The GEMM loaders address a 256-row tile with 32-bit byte offsets from a
@@ -330,43 +334,72 @@ int validate(const flce_problem_t* p) {
   return FLCE_OK;
 }
 
-// Width, in 256-row vocabulary tiles, of the backward pass's chunks.  A chunk
-// of ct tiles launches tiles_t * ceil(256 ct / 384) recompute tiles (depth H;
-// 256-row tiles for chunks under 384 rows) and ct * tiles_h dW tiles (depth
-// Tvp); a launch of n tiles runs in about ceil(n / CUs) rounds, one tile per
-// CU per round.  The dH contraction's cost does not depend on the split,
-// apart from its fp32 accumulator pass, which is counted with the launch
-// overhead as a fixed cost per chunk.  Among widths up to ct_max this picks
-// the one with the least estimated time (ties: the wider).  A round of
-// 384-row recompute tiles costs kWideRound 256-row rounds of the same depth:
-// 1.5 times the work at the 5-6% better rate measured on full rounds of the
-// recompute shape.
+// Width, in 256-row vocabulary tiles, of the backward pass's chunks, and the
+// tile of their dW.  A chunk of ct tiles launches tiles_t * ceil(256 ct / 384)
+// recompute tiles (depth H; 256-row tiles for chunks under 384 rows) and
+// either ct * tiles_h dW tiles (depth Tvp) or, with dW computed as Xc^T G on
+// 384-row tiles, ct * ceil(H / 384) of them; a launch of n tiles runs in
+// about ceil(n / CUs) rounds, one tile per CU per round.  The dH
+// contraction's cost does not depend on the split, apart from its fp32
+// accumulator pass, which is counted with the launch overhead as a fixed cost
+// per chunk.  For each dW tile this picks, among widths up to ct_max, the one
+// with the least estimated time (ties: the wider); the 384-row dW tiles are
+// taken when they save at least 1%, or when the caller fixes the tile
+// (dw_tile 256 or 384; 0 leaves it to the estimate).  A round of 384-row tiles costs
+// kWideRound 256-row rounds of the same depth: 1.5 times the work at the 5-6%
+// better rate measured on full rounds of the recompute shape.  On token
+// counts of 32768 and more the dW contraction is deep enough for the rate
+// gain measured on long contractions (about 10% on full rounds of dH's
+// shape): kWideRoundDeep.  Measured against 256-row dW tiles at the same
+// chunk width: 1.8% less time per step on T=8192, H=3072 (8 hidden tiles of
+// 384), 1.0% on T=65536, H=8192; 1.3% more on T=4096, H=4096, where 11 x 96
+// tiles take 5 rounds against 16 x 96 in 6 (which this model declines).
 constexpr int64_t kChunkOverheadDepth = 1536;  // per chunk, in units of one round's depth
 constexpr double kWideRound = 1.42;
-int64_t pick_chunk_tiles(int64_t Vu, int64_t tiles_t, int64_t tiles_h, int64_t H, int64_t Tvp, int64_t ct_max,
-                         int n_cu) {
+constexpr double kWideRoundDeep = 1.36;
+constexpr double kWideDwMargin = 0.99;
+struct ChunkChoice {
+  int64_t ct;
+  bool dw_wide;
+};
+ChunkChoice pick_chunks(int64_t Vu, int64_t tiles_t, int64_t tiles_h, int64_t H, int64_t Hp, int64_t Tvp,
+                        int64_t ct_max, int n_cu, int dw_tile) {
   const int64_t tiles_v = ceil_div(Vu, 256);
-  auto cost = [&](int64_t ct) {
+  const int64_t tiles_wh = ceil_div(H, gemm::WBM);
+  const double k_dw = Tvp >= 32768 ? kWideRoundDeep : kWideRound;
+  auto cost = [&](int64_t ct, bool wide) {
     const int64_t full = tiles_v / ct;
     const int64_t rem = tiles_v - full * ct;
     auto chunk = [&](int64_t c, int64_t rows) {
       const double rec = rows >= gemm::WBM
-                             ? (double)ceil_div(ceil_div(rows, gemm::WBM) * tiles_t, n_cu) * H * kWideRound
-                             : (double)ceil_div(tiles_t * c, n_cu) * H;
-      return rec + (double)(ceil_div(c * tiles_h, n_cu) * Tvp + kChunkOverheadDepth);
+                             ? (double)ceil_div(ceil_div(rows, gemm::WBM) * tiles_t, n_cu) * Hp * kWideRound
+                             : (double)ceil_div(tiles_t * c, n_cu) * Hp;
+      const double dw = wide ? (double)ceil_div(c * tiles_wh, n_cu) * Tvp * k_dw
+                             : (double)(ceil_div(c * tiles_h, n_cu) * Tvp);
+      return rec + dw + (double)kChunkOverheadDepth;
     };
     return full * chunk(ct, ct * 256) + (rem ? chunk(rem, Vu - full * ct * 256) : 0.0);
   };
-  int64_t best = ct_max;
-  double best_cost = cost(ct_max);
-  for (int64_t ct = ct_max - 1; ct >= 1; --ct) {
-    const double c = cost(ct);
-    if (c < best_cost) {
-      best = ct;
-      best_cost = c;
+  auto best_width = [&](bool wide, double& best_cost) {
+    int64_t best = ct_max;
+    best_cost = cost(ct_max, wide);
+    for (int64_t ct = ct_max - 1; ct >= 1; --ct) {
+      const double c = cost(ct, wide);
+      if (c < best_cost) {
+        best = ct;
+        best_cost = c;
+      }
     }
+    return best;
+  };
+  double narrow_cost = 0.0, wide_cost = 0.0;
+  if (dw_tile == 384) return {best_width(true, wide_cost), true};
+  const int64_t ct_narrow = best_width(false, narrow_cost);
+  if (dw_tile == 0 && H >= gemm::WBM) {
+    const int64_t ct_wide = best_width(true, wide_cost);
+    if (wide_cost < kWideDwMargin * narrow_cost) return {ct_wide, true};
   }
-  return best;
+  return {ct_narrow, false};
 }
 
 // Whether a chunk's dH runs on 384-row token tiles (it needs at least 384
@@ -414,8 +447,11 @@ Plan make_plan(const flce_problem_t* p, int n_cu = 256) {
   // sized for the widest chunk, so the workspace does not depend on the
   // device.
   const int64_t ct_max = std::max<int64_t>(1, pl.Vu / 1024);
-  const int64_t ct = pick_chunk_tiles(pl.Vu, pl.tiles_t, pl.tiles_h, pl.Hp, pl.Tvp, ct_max, n_cu);
+  const int dw_tile = (p->flags & FLCE_FLAG_DW_TILE_384) ? 384 : (p->flags & FLCE_FLAG_DW_TILE_256) ? 256 : 0;
+  const ChunkChoice cc = pick_chunks(pl.Vu, pl.tiles_t, pl.tiles_h, pl.H, pl.Hp, pl.Tvp, ct_max, n_cu, dw_tile);
+  const int64_t ct = cc.ct;
   pl.vc = ct * 256;
+  pl.dw_wide = cc.dw_wide;
   pl.n_cu = n_cu;
   pl.nchunks = ceil_div(pl.tiles_v, ct);
 
@@ -826,8 +862,10 @@ int flce_backward(const flce_problem_t* problem, const void* hidden, const void*
     // 2. dH_acc (+)= G W[v0 : v0 + vw]   (M = tokens, N = H, K = chunk rows) and
     //    dW[v0 : v0 + vw] = G^T Xc          (M = chunk rows, N = H, K = tokens)
     //    in one launch, dH's tiles first.  dH's K-major G and MN-major W, on
-    //    384-row token tiles when there are at least 384 token rows; dW reads
-    //    G MN-major (transposing LDS reads) and Xc K-major from XcT.
+    //    384-row token tiles when there are at least 384 token rows.  dW reads
+    //    G MN-major (transposing LDS reads) and Xc K-major from XcT; with
+    //    dw_wide it runs as dW^T = Xc^T G on 384-row tiles over the hidden
+    //    columns (XcT K-major, G's chunk rows as columns), stored transposed.
     {
       const int64_t tiles_hm = wide_h ? ceil_div(pl.Tvp, gemm::WBM) : pl.tiles_t;
       gemm::Operand Ah{G, pl.vc, (int)pl.Tvp - 1, 0};
@@ -836,23 +874,44 @@ int flce_backward(const flce_problem_t* problem, const void* hidden, const void*
       int mode = 0;
       if (c == 0) mode |= epi::kAccFirst;
       if (c == pl.nchunks - 1) mode |= epi::kAccLast;
-      gemm::Operand Aw{G, pl.vc, (int)pl.vc - 1, (int)pl.Tvp - 1};
-      gemm::Operand Bw{xct, pl.Tvp, (int)pl.H - 1, 0};
-      gemm::Schedule sw{(int)tiles_c, (int)pl.tiles_h, 0, tv, 3};
-      epi::StoreF32::Params ew{d_weight + v0 * pl.H, pl.H, (int)vw, (int)pl.H};
       const int64_t n_h = align_up((size_t)(tiles_hm * pl.tiles_h), 8);
-      const dim3 grid(n_h + tiles_c * pl.tiles_h);
       TraceScope tr(FLCE_KERNEL_DGRAD, 2.0 * chunk_flops, stream);
-      if (wide_h) {
-        using EH = epi::AccumH<gemm::WMB>;
-        EH::Params eh{hacc, pl.H, (bf16*)d_hidden, valid_idx, tv, (int)pl.H, mode};
-        hipLaunchKernelGGL((gemm::gemm_pair_wide<EH, epi::StoreF32>), grid, dim3(gemm::NTHREADS), 0, stream, Ah,
-                           Bh, sh, eh, (int)n_h, Aw, Bw, sw, ew);
+      if (pl.dw_wide) {
+        using EW = epi::StoreF32T<gemm::WMB>;
+        const int64_t tiles_wh = ceil_div(pl.H, gemm::WBM);
+        gemm::Operand Aw{xct, pl.Tvp, (int)pl.H - 1, 0};
+        gemm::Operand Bw{G, pl.vc, (int)pl.vc - 1, (int)pl.Tvp - 1};
+        gemm::Schedule sw{(int)tiles_wh, (int)tiles_c, 0, tv, 3};
+        EW::Params ew{d_weight + v0 * pl.H, pl.H, (int)vw, (int)pl.H};
+        const dim3 grid(n_h + tiles_wh * tiles_c);
+        if (wide_h) {
+          using EH = epi::AccumH<gemm::WMB>;
+          EH::Params eh{hacc, pl.H, (bf16*)d_hidden, valid_idx, tv, (int)pl.H, mode};
+          hipLaunchKernelGGL((gemm::gemm_pair_wide<EH, EW, true>), grid, dim3(gemm::NTHREADS), 0, stream, Ah, Bh,
+                             sh, eh, (int)n_h, Aw, Bw, sw, ew);
+        } else {
+          using EH = epi::AccumH<>;
+          EH::Params eh{hacc, pl.H, (bf16*)d_hidden, valid_idx, tv, (int)pl.H, mode};
+          hipLaunchKernelGGL((gemm::gemm_pair_nt<EH, EW>), grid, dim3(gemm::NTHREADS), 0, stream, Ah, Bh, sh, eh,
+                             (int)n_h, Aw, Bw, sw, ew);
+        }
       } else {
-        using EH = epi::AccumH<>;
-        EH::Params eh{hacc, pl.H, (bf16*)d_hidden, valid_idx, tv, (int)pl.H, mode};
-        hipLaunchKernelGGL((gemm::gemm_pair<true, false, EH, false, true, epi::StoreF32>), grid,
-                           dim3(gemm::NTHREADS), 0, stream, Ah, Bh, sh, eh, (int)n_h, Aw, Bw, sw, ew);
+        gemm::Operand Aw{G, pl.vc, (int)pl.vc - 1, (int)pl.Tvp - 1};
+        gemm::Operand Bw{xct, pl.Tvp, (int)pl.H - 1, 0};
+        gemm::Schedule sw{(int)tiles_c, (int)pl.tiles_h, 0, tv, 3};
+        epi::StoreF32::Params ew{d_weight + v0 * pl.H, pl.H, (int)vw, (int)pl.H};
+        const dim3 grid(n_h + tiles_c * pl.tiles_h);
+        if (wide_h) {
+          using EH = epi::AccumH<gemm::WMB>;
+          EH::Params eh{hacc, pl.H, (bf16*)d_hidden, valid_idx, tv, (int)pl.H, mode};
+          hipLaunchKernelGGL((gemm::gemm_pair_wide<EH, epi::StoreF32>), grid, dim3(gemm::NTHREADS), 0, stream, Ah,
+                             Bh, sh, eh, (int)n_h, Aw, Bw, sw, ew);
+        } else {
+          using EH = epi::AccumH<>;
+          EH::Params eh{hacc, pl.H, (bf16*)d_hidden, valid_idx, tv, (int)pl.H, mode};
+          hipLaunchKernelGGL((gemm::gemm_pair<true, false, EH, false, true, epi::StoreF32>), grid,
+                             dim3(gemm::NTHREADS), 0, stream, Ah, Bh, sh, eh, (int)n_h, Aw, Bw, sw, ew);
+        }
       }
     }
   }

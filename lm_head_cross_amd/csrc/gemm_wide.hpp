@@ -386,14 +386,66 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_wide_kernel(Operand A, Opera
   Epi::apply(ep, acc, m0, a0, n0, s0);
 }
 
+// One 384 x 256 tile of a K-major x MN-major product whose K is the valid
+// tokens (sch.tok_dim == 3: ceil(Tv / 128) * 128 of them) or sch.k_steps:
+// dW^T = Xc^T G of a chunk, A = XcT (hidden rows, all present; the last tile
+// computed shifted down), B = G (the chunk's head rows as columns).  With no
+// valid tokens the tile is all zeros.
+template <class Epi>
+__device__ __forceinline__ void run_wide_kmn(const Operand& A, const Operand& B, const Schedule& sch,
+                                             const typename Epi::Params& ep, int pid, bf16* s0, bf16* s1,
+                                             bf16* s2, bf16* s3) {
+  if (pid >= sch.tiles_m * sch.tiles_n) return;
+  int k_steps = sch.k_steps;
+  if (sch.tok_dim == 3) {
+    const int tv = *sch.tok_count;
+    k_steps = (tv + NST * BK - 1) / (NST * BK) * NST;
+  }
+  int tm, tn;
+  tile_of_wide(pid, sch.tiles_m, sch.tiles_n, tm, tn);
+  const int m0 = tm * WBM;
+  const int a0 = min(m0, A.mn_max + 1 - WBM);
+  const int n0 = tn * BN;
+  f32x16 acc[WMB][4];
+  if (k_steps > 0) {
+    mainloop_kmn(A, B, a0, n0, k_steps, s0, s1, s2, s3, acc);
+  } else {
+#pragma unroll
+    for (int i = 0; i < WMB; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  }
+  Epi::apply(ep, acc, m0, a0, n0, s0);
+}
+
+// dH of a chunk on 256-row token tiles (run_tile's K-major G x MN-major W)
+// and its dW as 384-row tiles of dW^T (run_wide_kmn) in one launch;
+// workgroups [0, n1) take dH's tiles, as in gemm_pair.
+template <class Epi1, class Epi2>
+__global__ __launch_bounds__(NTHREADS, 1) void gemm_pair_nt(Operand A1, Operand B1, Schedule sch1,
+                                                             typename Epi1::Params ep1, int n1, Operand A2,
+                                                             Operand B2, Schedule sch2, typename Epi2::Params ep2) {
+  __shared__ __attribute__((aligned(1024))) bf16 s0[WSTAGE_A];
+  __shared__ __attribute__((aligned(1024))) bf16 s1[STAGE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 s2[WSTAGE_A];
+  __shared__ __attribute__((aligned(1024))) bf16 s3[STAGE_ELEMS];
+  const int pid = blockIdx.x;
+  if (pid < n1) {
+    if (pid < sch1.tiles_m * sch1.tiles_n) run_tile<true, false, Epi1>(A1, B1, sch1, ep1, pid, s0, s1, s2, s3);
+  } else {
+    run_wide_kmn<Epi2>(A2, B2, sch2, ep2, pid - n1, s0, s1, s2, s3);
+  }
+}
+
 // dH of one chunk (K-major G x MN-major W with 384-row token tiles) and dW
 // of the chunk (run_tile's MN-major G x K-major XcT, 256-row tiles) in one
 // launch.  Workgroups [0, n1) take dH's tiles (n1: its host-side tile count
 // rounded up to a multiple of 8, so that dW's tiles keep the id-to-XCD
 // mapping tile_of assumes), the rest dW's.  Only the ceil(Tv / 384) token
 // tiles that hold valid tokens run; the last is computed shifted down to
-// end at row Tvp - 1 (G's rows past Tv are zero).
-template <class Epi1, class Epi2>
+// end at row Tvp - 1 (G's rows past Tv are zero).  With WIDE2, dW runs as
+// 384-row tiles of dW^T (run_wide_kmn) instead.
+template <class Epi1, class Epi2, bool WIDE2 = false>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_pair_wide(Operand A1, Operand B1, Schedule sch1,
                                                                typename Epi1::Params ep1, int n1, Operand A2,
                                                                Operand B2, Schedule sch2, typename Epi2::Params ep2) {
@@ -415,6 +467,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_pair_wide(Operand A1, Operan
     f32x16 acc[WMB][4];
     mainloop_kmn(A1, B1, a0, n0, sch1.k_steps, s0, s1, s2, s3, acc);
     Epi1::apply(ep1, acc, m0, a0, n0, s0);
+  } else if constexpr (WIDE2) {
+    run_wide_kmn<Epi2>(A2, B2, sch2, ep2, pid - n1, s0, s1, s2, s3);
   } else {
     run_tile<false, true, Epi2>(A2, B2, sch2, ep2, pid - n1, s0, s1, s2, s3);
   }

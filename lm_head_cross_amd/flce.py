@@ -39,17 +39,23 @@ def _raise_for(code: int, what: str) -> None:
 _WEIGHT_DTYPES = {torch.bfloat16: _lib.FLCE_DTYPE_BF16, torch.float32: _lib.FLCE_DTYPE_FP32}
 
 
+_DW_TILE_FLAGS = {None: 0, 256: _lib.FLCE_FLAG_DW_TILE_256, 384: _lib.FLCE_FLAG_DW_TILE_384}
+
+
 def make_problem(num_tokens: int, hidden: int, vocab: int, unpadded_vocab: int | None = None,
                  softcap: float = 0.0, ignore_index: int = -100, reduction: str = "sum",
                  num_label_tokens: int | None = None, weight_dtype=torch.bfloat16,
-                 round_head_on_load: bool = False) -> _lib.Problem:
+                 round_head_on_load: bool = False, dw_tile: int | None = None) -> _lib.Problem:
     """Fill an ``flce_problem_t``; value checks are the library's.  With
     ``weight_dtype=torch.float32`` the calls take the fp32 head and round its
     usable rows to bf16 themselves: staged in the workspace, or with
     ``round_head_on_load`` inside the GEMMs' tile loads (smaller workspace,
-    slower; see include/flce.h)."""
+    slower; see include/flce.h).  ``dw_tile`` (256 or 384) fixes the tile of
+    the backward's dW contraction, which the library otherwise picks."""
     if weight_dtype not in _WEIGHT_DTYPES:
         raise NotImplementedError(f"the head must be bfloat16 or float32, got {weight_dtype}")
+    if dw_tile not in _DW_TILE_FLAGS:
+        raise ValueError(f"dw_tile must be None, 256 or 384, got {dw_tile!r}")
     if reduction not in _REDUCTIONS:
         raise ValueError(f"reduction must be one of {sorted(_REDUCTIONS)}, got {reduction!r}")
     if num_label_tokens is not None and int(num_label_tokens) < 0:
@@ -60,7 +66,7 @@ def make_problem(num_tokens: int, hidden: int, vocab: int, unpadded_vocab: int |
         softcap=float(softcap), reduction=_REDUCTIONS[reduction], ignore_index=int(ignore_index),
         num_label_tokens=-1 if num_label_tokens is None else int(num_label_tokens),
         weight_dtype=_WEIGHT_DTYPES[weight_dtype],
-        flags=_lib.FLCE_FLAG_ROUND_HEAD_ON_LOAD if round_head_on_load else 0)
+        flags=(_lib.FLCE_FLAG_ROUND_HEAD_ON_LOAD if round_head_on_load else 0) | _DW_TILE_FLAGS[dw_tile])
 
 
 def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:

@@ -42,20 +42,21 @@ def dev():
     return torch.device("cuda:0")
 
 
-def problem_of(inp, weight_dtype=torch.bfloat16, round_on_load=False):
+def problem_of(inp, weight_dtype=torch.bfloat16, round_on_load=False, dw_tile=None):
     X, W = inp["hidden"], inp["weight"]
     return L.make_problem(X.shape[0], X.shape[1], W.shape[0], inp["unpadded_vocab"], inp["softcap"],
                           inp["ignore_index"], inp["reduction"], inp["num_label_tokens"], weight_dtype,
-                          round_head_on_load=round_on_load)
+                          round_head_on_load=round_on_load, dw_tile=dw_tile)
 
 
 def run_hip(inp, grad_out=1.0, dx_rows=None, dw_rows=None, keep_device=False, fp32_head_direct=False,
-            round_on_load=False):
+            round_on_load=False, dw_tile=None):
     """Forward + backward through the C ABI.  Returns CPU results; dX / dW
     are restricted to the given rows (all when None).  An fp32 head is rounded
     by flce_round_to_bf16 first, or with ``fp32_head_direct`` handed to the
     calls as fp32 (the library stages the rounded rows itself, or with
-    ``round_on_load`` rounds them inside the GEMMs' tile loads)."""
+    ``round_on_load`` rounds them inside the GEMMs' tile loads).  ``dw_tile``
+    fixes the dW contraction's tile (256 or 384 rows)."""
     d = dev()
     X = inp["hidden"].to(d)
     W = inp["weight"].to(d)
@@ -63,7 +64,8 @@ def run_hip(inp, grad_out=1.0, dx_rows=None, dw_rows=None, keep_device=False, fp
     direct = fp32_head_direct and W.dtype == torch.float32
     if W.dtype == torch.float32 and not direct:
         W = L.flce_round_to_bf16(W)
-    p = problem_of(inp, torch.float32 if direct else torch.bfloat16, round_on_load=direct and round_on_load)
+    p = problem_of(inp, torch.float32 if direct else torch.bfloat16, round_on_load=direct and round_on_load,
+                   dw_tile=dw_tile)
     T, H, V = p.num_tokens, p.hidden, p.vocab
     ws = L.alloc_workspace(p, d)
     loss = torch.empty((), dtype=torch.float32, device=d)

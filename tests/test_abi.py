@@ -91,6 +91,16 @@ def test_fp32_head_workspace():
     assert d[0] == e[0] == _lib.FLCE_OK and d[1] == e[1]
 
 
+def test_dw_tile_flags_leave_the_workspace_alone():
+    """Fixing the dW tile changes the launch plan, not the workspace (sized
+    for the widest chunk the planner may take)."""
+    for shape in ((4096, 4096, 128256, 128256), (8192, 3072, 262144, 256000), (700, 400, 2000, 1900)):
+        sizes = {_ws(make_problem(*shape, dw_tile=t)) for t in (None, 256, 384)}
+        assert len(sizes) == 1 and next(iter(sizes))[0] == _lib.FLCE_OK
+    with pytest.raises(ValueError):
+        make_problem(64, 512, 1000, dw_tile=128)
+
+
 def test_unaligned_hidden_stages_a_padded_head():
     """H a multiple of 8 but not of 128: the head's usable rows are staged
     with rows of Hp = ceil(H/128)*128 elements; the fp32 accumulator of dH
@@ -135,8 +145,10 @@ def test_library_source_allocates_no_device_memory():
     (dict(hidden=12), _lib.FLCE_ERR_UNSUPPORTED),
     (dict(hidden=4100), _lib.FLCE_ERR_UNSUPPORTED),
     (dict(weight_dtype=7), _lib.FLCE_ERR_UNSUPPORTED),
-    (dict(flags=2), _lib.FLCE_ERR_INVALID_ARG),
+    (dict(flags=8), _lib.FLCE_ERR_INVALID_ARG),
     (dict(flags=1), _lib.FLCE_ERR_INVALID_ARG),  # rounding on load needs an fp32 head
+    (dict(flags=6), _lib.FLCE_ERR_INVALID_ARG),  # both dW tiles
+    (dict(flags=4), _lib.FLCE_ERR_INVALID_ARG),  # 384-row dW tiles need H >= 384
     # 32-bit tile offsets: beyond these sizes the call is refused
     (dict(num_tokens=(1 << 21) + 1), _lib.FLCE_ERR_UNSUPPORTED),
     (dict(vocab=(1 << 23) + 8, unpadded_vocab=1000), _lib.FLCE_ERR_UNSUPPORTED),

@@ -54,6 +54,10 @@ SMALL = {
     # forward and recompute tiles, a straddling tile and NaN-free padding
     "vocab_300_softcap": _small(112, T=300, H=128, V=383, Vu=300, w_std=0.5, pad_std=30.0, softcap=30.0,
                                 ignore_frac=0.05),
+    # hidden sizes for the 384-row dW^T tiles: one tile shifted down over all
+    # but 16 rows of the first; three whole tiles and several chunks
+    "hidden_400": _small(113, T=700, H=400, V=2000, Vu=1900, w_std=0.05, softcap=30.0, ignore_frac=0.1),
+    "hidden_1152_chunks": _small(114, T=520, H=1152, V=5000, Vu=4800, w_std=0.03, ignore_frac=0.05),
 }
 
 
@@ -65,6 +69,42 @@ def test_small_full_parity(name):
     res = run_hip(inp)
     assert res["status"] == 0
     check_full(inp, res, label=name)
+
+
+DW_384 = [k for k, w in SMALL.items() if w.H >= 384]
+
+
+@pytest.mark.parametrize("name", DW_384)
+def test_small_full_parity_dw_tile_384(name):
+    """dW on 384-row tiles of Xc^T G (stored transposed), which the library
+    picks by itself only where rounds of tiles on the device favour it."""
+    w = SMALL[name]
+    say(f"case {name}: T={w.T} H={w.H} V={w.V} Vu={w.Vu}, dW tile 384")
+    inp = make_inputs(w)
+    res = run_hip(inp, dw_tile=384)
+    assert res["status"] == 0
+    check_full(inp, res, label=name)
+    # Against 256-row dW tiles: dX takes the same kernels (bit for bit); dW
+    # sums the same products over tokens in the same order.
+    ref = run_hip(inp, dw_tile=256)
+    for k in ("lse", "token_loss", "dX"):
+        assert torch.equal(res[k], ref[k]), k
+    same = torch.equal(res["dW"], ref["dW"])
+    say(f"  dW bitwise equal to the 256-row tiles: {same}")
+    torch.testing.assert_close(res["dW"], ref["dW"], rtol=1e-5, atol=1e-7)
+
+
+@pytest.mark.parametrize("dw_tile", [256, 384])
+def test_all_positions_ignored_wide_hidden(dw_tile):
+    """No valid token with H >= 384: dW's contraction over tokens is empty
+    and every stored row must be exactly zero, on either dW tile."""
+    inp = make_inputs(SMALL["hidden_400"])
+    T = inp["hidden"].shape[0]
+    c = dict(inp)
+    c["labels"] = torch.full((T,), -100, dtype=torch.int64)
+    res = run_hip(c, dw_tile=dw_tile)
+    assert res["status"] == 0 and res["loss"] == 0.0
+    assert torch.all(res["dX"] == 0) and torch.all(res["dW"] == 0)
 
 
 def test_fp32_head_handed_over_directly():
