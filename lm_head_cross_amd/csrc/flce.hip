@@ -345,18 +345,19 @@ int validate(const flce_problem_t* p) {
 // per chunk.  For each dW tile this picks, among widths up to ct_max, the one
 // with the least estimated time (ties: the wider); the 384-row dW tiles are
 // taken when they save at least 1%, or when the caller fixes the tile
-// (dw_tile 256 or 384; 0 leaves it to the estimate).  A round of 384-row tiles costs
-// kWideRound 256-row rounds of the same depth: 1.5 times the work at the 5-6%
-// better rate measured on full rounds of the recompute shape.  On token
-// counts of 32768 and more the dW contraction is deep enough for the rate
-// gain measured on long contractions (about 10% on full rounds of dH's
-// shape): kWideRoundDeep.  Measured against 256-row dW tiles at the same
-// chunk width: 1.8% less time per step on T=8192, H=3072 (8 hidden tiles of
-// 384), 1.0% on T=65536, H=8192; 1.3% more on T=4096, H=4096, where 11 x 96
-// tiles take 5 rounds against 16 x 96 in 6 (which this model declines).
+// (dw_tile 256 or 384; 0 leaves it to the estimate).  A round of 384-row
+// recompute tiles costs kWideRound 256-row rounds of the same depth: 1.5
+// times the work at the 5-6% better rate measured on full rounds of the
+// recompute shape.  A round of 384-row dW^T tiles costs kWideRoundDw,
+// calibrated on four head shapes (each measured with both dW tiles at the
+// width this estimate picks for each, same box, alternating runs): per step,
+// T=8192, H=3072 39.6 -> 37.7 ms with the 384-row tiles, T=16384 (8192
+// valid), H=5120 40.6 -> 39.7, T=65536, H=8192 424.4 -> 419.8, and T=4096,
+// H=4096 13.02 against 13.04 (a tie, which the 1% margin leaves on 256-row
+// tiles).
 constexpr int64_t kChunkOverheadDepth = 1536;  // per chunk, in units of one round's depth
 constexpr double kWideRound = 1.42;
-constexpr double kWideRoundDeep = 1.36;
+constexpr double kWideRoundDw = 1.38;
 constexpr double kWideDwMargin = 0.99;
 struct ChunkChoice {
   int64_t ct;
@@ -366,7 +367,6 @@ ChunkChoice pick_chunks(int64_t Vu, int64_t tiles_t, int64_t tiles_h, int64_t H,
                         int64_t ct_max, int n_cu, int dw_tile) {
   const int64_t tiles_v = ceil_div(Vu, 256);
   const int64_t tiles_wh = ceil_div(H, gemm::WBM);
-  const double k_dw = Tvp >= 32768 ? kWideRoundDeep : kWideRound;
   auto cost = [&](int64_t ct, bool wide) {
     const int64_t full = tiles_v / ct;
     const int64_t rem = tiles_v - full * ct;
@@ -374,7 +374,7 @@ ChunkChoice pick_chunks(int64_t Vu, int64_t tiles_t, int64_t tiles_h, int64_t H,
       const double rec = rows >= gemm::WBM
                              ? (double)ceil_div(ceil_div(rows, gemm::WBM) * tiles_t, n_cu) * Hp * kWideRound
                              : (double)ceil_div(tiles_t * c, n_cu) * Hp;
-      const double dw = wide ? (double)ceil_div(c * tiles_wh, n_cu) * Tvp * k_dw
+      const double dw = wide ? (double)ceil_div(c * tiles_wh, n_cu) * Tvp * kWideRoundDw
                              : (double)(ceil_div(c * tiles_h, n_cu) * Tvp);
       return rec + dw + (double)kChunkOverheadDepth;
     };
