@@ -133,6 +133,9 @@ def main():
     ap.add_argument("--dw-tile", type=int, choices=(256, 384), default=None,
                     help="fix the tile of the backward's dW contraction (FLCE_FLAG_DW_TILE_256 / _384); by "
                          "default the library picks it")
+    ap.add_argument("--restage-head", action="store_true",
+                    help="with --fp32-head-direct: the backward stages the head again instead of reusing the "
+                         "forward's staged copy in the same workspace (FLCE_FLAG_HEAD_STAGED)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -160,7 +163,8 @@ def main():
     T, H, V, Vu = w.T, w.H, w.V, w.Vu
     Tv = inp["n_valid"]
     p = L.make_problem(T, H, V, Vu, w.softcap, inp["ignore_index"], w.reduction, inp["num_label_tokens"],
-                       W.dtype, round_head_on_load=direct and args.round_head_on_load, dw_tile=args.dw_tile)
+                       W.dtype, round_head_on_load=direct and args.round_head_on_load, dw_tile=args.dw_tile,
+                       head_staged=not args.restage_head)
     ws = L.alloc_workspace(p, dev)
     loss = torch.empty((), dtype=torch.float32, device=dev)
     lse = torch.empty(T, dtype=torch.float32, device=dev)
@@ -335,6 +339,7 @@ def main():
             + (" (rounded on load)" if direct and args.round_head_on_load else ""),
             "num_label_tokens": inp["num_label_tokens"],
             "dw_tile": args.dw_tile or "library's choice",
+            "backward_restages_head": bool(args.restage_head),
             "credited_tflop_per_step": round(credited / 1e12, 3),
             "model_tflop_per_step": round(6.0 * Tv * Vu * H / 1e12, 3),
             "label_tokens_per_s": round(Tv / (ms * 1e-3), 1),

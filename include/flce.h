@@ -127,7 +127,19 @@ typedef enum flce_dtype {
  *                   tiles on the device's compute units: 256-row tiles of
  *                   G^T Xc, or 384-row tiles of Xc^T G stored transposed.
  *                   Either gives the same result up to the order of fp32
- *                   rounding.  Other bits are invalid.
+ *                   rounding.  FLCE_FLAG_HEAD_STAGED, read by flce_backward
+ *                   only (flce_forward accepts and ignores it, so one problem
+ *                   can serve both calls): the caller asserts that the
+ *                   workspace still holds the head copy that the matching
+ *                   flce_forward staged in it (an fp32 head, or H not a
+ *                   multiple of 128), with the same problem and head and
+ *                   nothing written to the workspace since; the backward
+ *                   then skips its own staging pass (one read of the head's
+ *                   usable rows).  Without a staged copy the bit changes
+ *                   nothing.  Not for a workspace other than the forward's
+ *                   (flce_forward_noalloc stages into its own scratch): the
+ *                   backward would read whatever the region holds.  Other
+ *                   bits are invalid.
  */
 typedef struct flce_problem {
   int64_t num_tokens;
@@ -146,6 +158,7 @@ typedef struct flce_problem {
 #define FLCE_FLAG_ROUND_HEAD_ON_LOAD 1
 #define FLCE_FLAG_DW_TILE_256 2
 #define FLCE_FLAG_DW_TILE_384 4
+#define FLCE_FLAG_HEAD_STAGED 8
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* flce_status_string(int status);

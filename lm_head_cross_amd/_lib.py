@@ -24,6 +24,7 @@ FLCE_DTYPE_FP32 = 1
 FLCE_FLAG_ROUND_HEAD_ON_LOAD = 1
 FLCE_FLAG_DW_TILE_256 = 2
 FLCE_FLAG_DW_TILE_384 = 4
+FLCE_FLAG_HEAD_STAGED = 8
 
 EXPORTED = ("flce_status_string", "flce_version", "flce_workspace_size", "flce_forward", "flce_forward_noalloc",
             "flce_backward",

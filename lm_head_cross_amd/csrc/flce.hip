@@ -318,7 +318,8 @@ int validate(const flce_problem_t* p) {
   if (p->reduction != FLCE_REDUCTION_SUM && p->reduction != FLCE_REDUCTION_MEAN) return FLCE_ERR_INVALID_ARG;
   if (p->num_label_tokens == 0) return FLCE_ERR_INVALID_ARG;
   if (p->weight_dtype != FLCE_DTYPE_BF16 && p->weight_dtype != FLCE_DTYPE_FP32) return FLCE_ERR_UNSUPPORTED;
-  if ((p->flags & ~(FLCE_FLAG_ROUND_HEAD_ON_LOAD | FLCE_FLAG_DW_TILE_256 | FLCE_FLAG_DW_TILE_384)) != 0)
+  if ((p->flags & ~(FLCE_FLAG_ROUND_HEAD_ON_LOAD | FLCE_FLAG_DW_TILE_256 | FLCE_FLAG_DW_TILE_384 |
+                    FLCE_FLAG_HEAD_STAGED)) != 0)
     return FLCE_ERR_INVALID_ARG;
   if ((p->flags & FLCE_FLAG_DW_TILE_256) && (p->flags & FLCE_FLAG_DW_TILE_384)) return FLCE_ERR_INVALID_ARG;
   if ((p->flags & FLCE_FLAG_DW_TILE_384) && p->hidden < 384) return FLCE_ERR_INVALID_ARG;
@@ -776,7 +777,10 @@ int flce_backward(const flce_problem_t* problem, const void* hidden, const void*
   bf16* G = ws_at<bf16>(workspace, pl.off_g);
   float* hacc = ws_at<float>(workspace, pl.off_hacc);
   const int* tv = &meta->n_valid;
-  const bf16* W = staged_head(pl, p, weight, workspace, stream);
+  // The head copy the matching forward staged (the caller vouches for it),
+  // or this call's own.
+  const bf16* W = (p.flags & FLCE_FLAG_HEAD_STAGED) && pl.stage_head ? ws_at<const bf16>(workspace, pl.off_wst)
+                                                                      : staged_head(pl, p, weight, workspace, stream);
 
   launch_compact_gather(pl, p, labels, hidden, meta, valid_idx, yc, device_status, nullptr, nullptr, xc, stream);
   bf16* xct = ws_at<bf16>(workspace, pl.off_xct);

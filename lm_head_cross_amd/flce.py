@@ -45,13 +45,17 @@ _DW_TILE_FLAGS = {None: 0, 256: _lib.FLCE_FLAG_DW_TILE_256, 384: _lib.FLCE_FLAG_
 def make_problem(num_tokens: int, hidden: int, vocab: int, unpadded_vocab: int | None = None,
                  softcap: float = 0.0, ignore_index: int = -100, reduction: str = "sum",
                  num_label_tokens: int | None = None, weight_dtype=torch.bfloat16,
-                 round_head_on_load: bool = False, dw_tile: int | None = None) -> _lib.Problem:
+                 round_head_on_load: bool = False, dw_tile: int | None = None,
+                 head_staged: bool = False) -> _lib.Problem:
     """Fill an ``flce_problem_t``; value checks are the library's.  With
     ``weight_dtype=torch.float32`` the calls take the fp32 head and round its
     usable rows to bf16 themselves: staged in the workspace, or with
     ``round_head_on_load`` inside the GEMMs' tile loads (smaller workspace,
     slower; see include/flce.h).  ``dw_tile`` (256 or 384) fixes the tile of
-    the backward's dW contraction, which the library otherwise picks."""
+    the backward's dW contraction, which the library otherwise picks.
+    ``head_staged``: the backward reuses the head copy that the matching
+    forward staged in the same workspace (FLCE_FLAG_HEAD_STAGED; the caller
+    vouches that the workspace and head are untouched in between)."""
     if weight_dtype not in _WEIGHT_DTYPES:
         raise NotImplementedError(f"the head must be bfloat16 or float32, got {weight_dtype}")
     if dw_tile not in _DW_TILE_FLAGS:
@@ -66,7 +70,8 @@ def make_problem(num_tokens: int, hidden: int, vocab: int, unpadded_vocab: int |
         softcap=float(softcap), reduction=_REDUCTIONS[reduction], ignore_index=int(ignore_index),
         num_label_tokens=-1 if num_label_tokens is None else int(num_label_tokens),
         weight_dtype=_WEIGHT_DTYPES[weight_dtype],
-        flags=(_lib.FLCE_FLAG_ROUND_HEAD_ON_LOAD if round_head_on_load else 0) | _DW_TILE_FLAGS[dw_tile])
+        flags=(_lib.FLCE_FLAG_ROUND_HEAD_ON_LOAD if round_head_on_load else 0) | _DW_TILE_FLAGS[dw_tile]
+        | (_lib.FLCE_FLAG_HEAD_STAGED if head_staged else 0))
 
 
 def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:

@@ -42,21 +42,22 @@ def dev():
     return torch.device("cuda:0")
 
 
-def problem_of(inp, weight_dtype=torch.bfloat16, round_on_load=False, dw_tile=None):
+def problem_of(inp, weight_dtype=torch.bfloat16, round_on_load=False, dw_tile=None, head_staged=False):
     X, W = inp["hidden"], inp["weight"]
     return L.make_problem(X.shape[0], X.shape[1], W.shape[0], inp["unpadded_vocab"], inp["softcap"],
                           inp["ignore_index"], inp["reduction"], inp["num_label_tokens"], weight_dtype,
-                          round_head_on_load=round_on_load, dw_tile=dw_tile)
+                          round_head_on_load=round_on_load, dw_tile=dw_tile, head_staged=head_staged)
 
 
 def run_hip(inp, grad_out=1.0, dx_rows=None, dw_rows=None, keep_device=False, fp32_head_direct=False,
-            round_on_load=False, dw_tile=None):
+            round_on_load=False, dw_tile=None, head_staged=False):
     """Forward + backward through the C ABI.  Returns CPU results; dX / dW
     are restricted to the given rows (all when None).  An fp32 head is rounded
     by flce_round_to_bf16 first, or with ``fp32_head_direct`` handed to the
     calls as fp32 (the library stages the rounded rows itself, or with
     ``round_on_load`` rounds them inside the GEMMs' tile loads).  ``dw_tile``
-    fixes the dW contraction's tile (256 or 384 rows)."""
+    fixes the dW contraction's tile (256 or 384 rows); ``head_staged`` lets
+    the backward reuse the forward's staged head (same workspace)."""
     d = dev()
     X = inp["hidden"].to(d)
     W = inp["weight"].to(d)
@@ -65,7 +66,7 @@ def run_hip(inp, grad_out=1.0, dx_rows=None, dw_rows=None, keep_device=False, fp
     if W.dtype == torch.float32 and not direct:
         W = L.flce_round_to_bf16(W)
     p = problem_of(inp, torch.float32 if direct else torch.bfloat16, round_on_load=direct and round_on_load,
-                   dw_tile=dw_tile)
+                   dw_tile=dw_tile, head_staged=head_staged)
     T, H, V = p.num_tokens, p.hidden, p.vocab
     ws = L.alloc_workspace(p, d)
     loss = torch.empty((), dtype=torch.float32, device=d)

@@ -93,9 +93,10 @@ def test_fp32_head_workspace():
 
 def test_dw_tile_flags_leave_the_workspace_alone():
     """Fixing the dW tile changes the launch plan, not the workspace (sized
-    for the widest chunk the planner may take)."""
+    for the widest chunk the planner may take); so does reusing the
+    forward's staged head."""
     for shape in ((4096, 4096, 128256, 128256), (8192, 3072, 262144, 256000), (700, 400, 2000, 1900)):
-        sizes = {_ws(make_problem(*shape, dw_tile=t)) for t in (None, 256, 384)}
+        sizes = {_ws(make_problem(*shape, dw_tile=t, head_staged=h)) for t in (None, 256, 384) for h in (False, True)}
         assert len(sizes) == 1 and next(iter(sizes))[0] == _lib.FLCE_OK
     with pytest.raises(ValueError):
         make_problem(64, 512, 1000, dw_tile=128)
@@ -145,7 +146,7 @@ def test_library_source_allocates_no_device_memory():
     (dict(hidden=12), _lib.FLCE_ERR_UNSUPPORTED),
     (dict(hidden=4100), _lib.FLCE_ERR_UNSUPPORTED),
     (dict(weight_dtype=7), _lib.FLCE_ERR_UNSUPPORTED),
-    (dict(flags=8), _lib.FLCE_ERR_INVALID_ARG),
+    (dict(flags=16), _lib.FLCE_ERR_INVALID_ARG),
     (dict(flags=1), _lib.FLCE_ERR_INVALID_ARG),  # rounding on load needs an fp32 head
     (dict(flags=6), _lib.FLCE_ERR_INVALID_ARG),  # both dW tiles
     (dict(flags=4), _lib.FLCE_ERR_INVALID_ARG),  # 384-row dW tiles need H >= 384

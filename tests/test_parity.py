@@ -13,9 +13,10 @@ import numpy as np
 import pytest
 import torch
 
+import lm_head_cross_amd as L
 import oracle
 from tests.gpu_common import (TOL_GRAD_REL_L2, TOL_TOKEN_ABS, TOL_TOTAL_REL, check_full, check_rows,
-                              oracle_problem, rel_l2, run_hip, say, stored_lse)
+                              oracle_problem, problem_of, rel_l2, run_hip, say, stored_lse)
 from workloads import WORKLOADS, Workload, make_inputs, sample_rows
 
 pytestmark = pytest.mark.gpu
@@ -317,7 +318,6 @@ def test_out_of_range_labels_flagged_and_skipped():
 
 
 def test_empty_batch():
-    import lm_head_cross_amd as L
     d = torch.device("cuda:0")
     p = L.make_problem(0, 128, 1000, reduction="mean")
     X = torch.empty((0, 128), dtype=torch.bfloat16, device=d)
@@ -334,7 +334,6 @@ def test_empty_batch():
 
 
 def test_round_to_bf16_matches_oracle_rounding():
-    import lm_head_cross_amd as L
     rng = np.random.default_rng(3)
     a = np.concatenate([rng.standard_normal(100003).astype(np.float32),
                         ((rng.integers(0, 0x7F7F, 5000, dtype=np.uint32) << 16) | 0x8000).view(np.float32),
@@ -420,7 +419,6 @@ def test_no_logits_sized_allocation():
     """Forward + backward at the llama3-8b head shape with the outputs already
     allocated: the call's extra device memory (the workspace the binding
     allocates) stays below one bf16 [T, Vu] logits buffer."""
-    import lm_head_cross_amd as L
     w = WORKLOADS[2]
     d = torch.device("cuda:0")
     inp = make_inputs(w, device="cuda:0")
@@ -468,3 +466,35 @@ def test_single_usable_row(softcap):
     assert res["dX"].float().abs().max().item() <= 1e-5 * wmax
     assert res["dW"][:1].abs().max().item() <= 1e-5 * xmax * ref.n_valid
     assert torch.all(res["dW"][1:] == 0)
+
+
+@pytest.mark.parametrize("name,direct", [("fp32_head", True), ("hidden_328_fp32_head", True),
+                                         ("hidden_200", False), ("multichunk_sum_runs", False)])
+def test_backward_reuses_the_forward_staged_head(name, direct):
+    """FLCE_FLAG_HEAD_STAGED: the backward reads the head copy that the
+    forward staged in the same workspace.  With a staged copy (an fp32 head
+    handed over directly, or H not a multiple of 128) the backward is handed
+    a NaN head and must not read it; without one the bit changes nothing.
+    Either way the results equal the unflagged run bit for bit."""
+    d = torch.device("cuda:0")
+    inp = make_inputs(SMALL[name])
+    ref = run_hip(inp, fp32_head_direct=direct)
+    X, W, y = inp["hidden"].to(d), inp["weight"].to(d), inp["labels"].to(d)
+    if W.dtype == torch.float32 and not direct:
+        W = L.flce_round_to_bf16(W)
+    p = problem_of(inp, W.dtype, head_staged=True)
+    T, H, V = p.num_tokens, p.hidden, p.vocab
+    staged = W.dtype == torch.float32 or H % 128 != 0
+    ws = L.alloc_workspace(p, d)
+    loss = torch.empty((), dtype=torch.float32, device=d)
+    lse = torch.empty(T, dtype=torch.float32, device=d)
+    tl = torch.empty(T, dtype=torch.float32, device=d)
+    L.flce_forward(p, X, W, y, loss, lse, tl, None, ws)
+    Wb = torch.full_like(W, float("nan")) if staged else W
+    dX = torch.empty_like(X)
+    dW = torch.empty((V, H), dtype=torch.float32, device=d)
+    L.flce_backward(p, X, Wb, y, lse, torch.tensor(1.0, device=d), dX, dW, None, ws)
+    torch.cuda.synchronize()
+    assert loss.item() == ref["loss"]
+    assert torch.equal(lse.cpu(), ref["lse"]) and torch.equal(tl.cpu(), ref["token_loss"])
+    assert torch.equal(dX.cpu(), ref["dX"]) and torch.equal(dW.cpu(), ref["dW"])
