@@ -300,7 +300,8 @@ struct StoreF32 {
 // so each such group lies wholly inside or outside [m0, hcols).  Rows below
 // m0 (a last tile computed shifted down) belong to the tile before.  Plain
 // stores: the 32-byte pieces of 4 consecutive stores fill whole 128-byte
-// lines, which the L2 merges before they go out.
+// lines, which the L2 merges before they go out (streaming stores of the
+// same pieces made the dH + dW launch 6% slower at T=8192, H=3072).
 template <int MB>
 struct StoreF32T {
   struct Params {

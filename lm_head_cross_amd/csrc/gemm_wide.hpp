@@ -1,6 +1,7 @@
 // GEMMs with a 384 x 256 tile: the projection and the backward recompute
-// (both operands K-major, mainloop_w), and dH (K-major G x MN-major W,
-// mainloop_kmn).  Each of the 4 waves owns 192 x 128 of the tile as 6 x 4
+// (both operands K-major, mainloop_w), dH (K-major G x MN-major W,
+// mainloop_kmn) and dW computed transposed, dW^T = Xc^T G (K-major XcT x
+// MN-major G, mainloop_kmn).  Each of the 4 waves owns 192 x 128 of the tile as 6 x 4
 // blocks of v_mfma_f32_32x32x16_bf16.  Against the 256 x 256 tile, a k step
 // issues 24 MFMAs per 10 fragments (16 per 8), and a stage moves 80 KB into
 // LDS per 384 x 256 x 64 multiply-adds (64 KB per 256 x 256 x 64): about a
@@ -21,10 +22,11 @@
 // explicitly (acc_fence).
 //
 // Two LDS stages of 80 KB (A 48 KB, B 32 KB): the whole 160 KB of a CU.
-// Every tile is full: the last head tile (of the usable rows, or of a
-// chunk) is computed shifted down so that it ends at the last row, and the
-// epilogue drops the rows that belong to the tile before it.  The token
-// operand has whole 256-row tiles.
+// Every tile is full: the last 384-row tile (of the usable head rows, of a
+// chunk, of the valid tokens, or of the hidden columns) is computed shifted
+// down so that it ends at the last row, and the epilogue drops the rows that
+// belong to the tile before it.  The 256-wide operand has whole tiles, or is
+// clamped on load.
 #pragma once
 
 #include "gemm_tile.hpp"
