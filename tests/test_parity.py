@@ -498,3 +498,34 @@ def test_backward_reuses_the_forward_staged_head(name, direct):
     assert loss.item() == ref["loss"]
     assert torch.equal(lse.cpu(), ref["lse"]) and torch.equal(tl.cpu(), ref["token_loss"])
     assert torch.equal(dX.cpu(), ref["dX"]) and torch.equal(dW.cpu(), ref["dW"])
+
+
+def test_two_streams_at_once_equal_one_after_the_other():
+    """The library keeps no state between calls: two problems enqueued
+    interleaved on two streams (each with its own workspace), with no
+    synchronisation between them, give bit for bit the results of running
+    them one after the other on the default stream."""
+    d = torch.device("cuda:0")
+    cases = [make_inputs(SMALL["multichunk_sum_runs"]), make_inputs(SMALL["hidden_400"])]
+    refs = [run_hip(inp) for inp in cases]
+    runs = []
+    for inp in cases:
+        X, W, y = inp["hidden"].to(d), inp["weight"].to(d), inp["labels"].to(d)
+        p = problem_of(inp)
+        T, H, V = p.num_tokens, p.hidden, p.vocab
+        runs.append(dict(p=p, X=X, W=W, y=y, ws=L.alloc_workspace(p, d),
+                         loss=torch.empty((), device=d), lse=torch.empty(T, device=d),
+                         tl=torch.empty(T, device=d), g=torch.tensor(1.0, device=d),
+                         dX=torch.empty_like(X), dW=torch.empty((V, H), device=d)))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for r, s in zip(runs, streams):
+        L.flce_forward(r["p"], r["X"], r["W"], r["y"], r["loss"], r["lse"], r["tl"], None, r["ws"], stream=s)
+    for r, s in zip(runs, streams):
+        L.flce_backward(r["p"], r["X"], r["W"], r["y"], r["lse"], r["g"], r["dX"], r["dW"], None, r["ws"],
+                        stream=s)
+    torch.cuda.synchronize()
+    for r, ref in zip(runs, refs):
+        assert r["loss"].item() == ref["loss"]
+        assert torch.equal(r["lse"].cpu(), ref["lse"]) and torch.equal(r["tl"].cpu(), ref["token_loss"])
+        assert torch.equal(r["dX"].cpu(), ref["dX"]) and torch.equal(r["dW"].cpu(), ref["dW"])
