@@ -313,3 +313,28 @@ def test_one_class():
         counted = y != -100
         zc = z[counted, 0].float()
         assert torch.all((res["lse"][counted] - zc).abs() <= 1e-6 * (1 + zc.abs()))
+
+
+def _sweep_case(i):
+    rng = np.random.default_rng(9000 + i)
+    T = int(rng.choice([1, 2, 63, 64, 65, 255, 257] + [int(x) for x in rng.integers(1, 3001, 3)]))
+    V = int(rng.choice([1, 2, 3, 7, 8, 9, 15, 16, 17] + [int(x) for x in rng.integers(2, 20001, 5)]))
+    ignore_frac = float(rng.choice([0.0, 0.05, 0.5])) if T >= 20 else 0.0
+    return _small(f"ce{200 + i}", T=T, V=V, dtype=str(rng.choice(["bf16", "fp32"])),
+                  std=float(rng.choice([0.5, 2.0, 5.0])), ignore_frac=ignore_frac,
+                  reduction=str(rng.choice(["sum", "mean"])), use_mask=bool(rng.random() < 0.3),
+                  peak=float(rng.choice([0.0, 0.0, 10.0])))
+
+
+@pytest.mark.parametrize("i", range(32))
+def test_random_small_problem(i):
+    """A seeded sweep of random small problems (row lengths of every
+    alignment, so the scalar head and tail paths vary; bf16 and fp32; masks;
+    peaked labels) against the oracle, element by element."""
+    w = _sweep_case(i)
+    say(f"sweep {i}: T={w.T} V={w.V} {w.dtype} std={w.std} {w.reduction} ignore={w.ignore_frac} "
+        f"mask={w.use_mask} peak={w.peak}")
+    inp = make_logit_inputs(w)
+    res = _run(inp)
+    assert res["status"] == 0
+    _check_full(inp, res, label=f"sweep{i}")
