@@ -175,6 +175,21 @@ int flce_version(void);
 int flce_workspace_size(const flce_problem_t* problem, size_t* bytes);
 
 /*
+ * The backward pass's launch plan for this problem on a device with cu_count
+ * compute units (<= 0: the current device's count, 256 when it cannot be
+ * read): the vocabulary chunk width in head rows (*chunk_rows, a multiple of
+ * 256, at most max(256, a quarter of Vu)), the number of chunks (*chunks; 0
+ * for a problem with no tokens, where the backward launches no chunk) and the
+ * rows of the dW contraction's tiles (*dw_tile_rows: 256 for tiles of G^T Xc,
+ * 384 for tiles of Xc^T G stored transposed).  It follows the problem's
+ * FLCE_FLAG_DW_TILE_* bits.  Host only: launches nothing, and with
+ * cu_count > 0 makes no HIP call.  The workspace size does not depend on it.
+ * Errors: as flce_workspace_size; FLCE_ERR_INVALID_ARG for a NULL output.
+ */
+int flce_backward_plan(const flce_problem_t* problem, int cu_count, int64_t* chunk_rows, int64_t* chunks,
+                       int* dw_tile_rows);
+
+/*
  * Forward pass.
  *
  * hidden       bf16 [T, H], 16-byte aligned.

@@ -26,7 +26,8 @@ FLCE_FLAG_DW_TILE_256 = 2
 FLCE_FLAG_DW_TILE_384 = 4
 FLCE_FLAG_HEAD_STAGED = 8
 
-EXPORTED = ("flce_status_string", "flce_version", "flce_workspace_size", "flce_forward", "flce_forward_noalloc",
+EXPORTED = ("flce_status_string", "flce_version", "flce_workspace_size", "flce_backward_plan", "flce_forward",
+            "flce_forward_noalloc",
             "flce_backward",
             "flce_round_to_bf16", "flce_trace_start", "flce_trace_select", "flce_trace_stop", "flce_trace_count", "flce_trace_get",
             "chunked_ce_workspace_size", "chunked_ce_forward", "chunked_ce_backward", "chunked_ce_mask_labels")
@@ -90,6 +91,9 @@ def load() -> ctypes.CDLL:
     lib.flce_version.argtypes = []
     lib.flce_workspace_size.restype = ctypes.c_int
     lib.flce_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+    lib.flce_backward_plan.restype = ctypes.c_int
+    lib.flce_backward_plan.argtypes = [P, ctypes.c_int, ctypes.POINTER(ctypes.c_int64),
+                                       ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int)]
     lib.flce_forward.restype = ctypes.c_int
     lib.flce_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.flce_forward_noalloc.restype = ctypes.c_int

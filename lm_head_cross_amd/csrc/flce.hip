@@ -627,6 +627,18 @@ int flce_workspace_size(const flce_problem_t* problem, size_t* bytes) {
   return FLCE_OK;
 }
 
+int flce_backward_plan(const flce_problem_t* problem, int cu_count, int64_t* chunk_rows, int64_t* chunks,
+                       int* dw_tile_rows) {
+  const int st = validate(problem);
+  if (st != FLCE_OK) return st;
+  if (!chunk_rows || !chunks || !dw_tile_rows) return FLCE_ERR_INVALID_ARG;
+  const Plan pl = make_plan(problem, cu_count > 0 ? cu_count : device_cu_count());
+  *chunk_rows = pl.vc;
+  *chunks = problem->num_tokens == 0 ? 0 : pl.nchunks;
+  *dw_tile_rows = pl.dw_wide ? gemm::WBM : 256;
+  return FLCE_OK;
+}
+
 }  // extern "C"
 
 namespace flce {

@@ -108,6 +108,16 @@ def flce_workspace_size(problem: _lib.Problem) -> int:
     return int(out.value)
 
 
+def flce_backward_plan(problem, cu_count: int = 0) -> tuple[int, int, int]:
+    """The backward pass's plan: (chunk width in head rows, number of
+    chunks, rows of the dW tiles), for ``cu_count`` compute units (0: the
+    current device's); see include/flce.h."""
+    rows, n, tile = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int(0)
+    _raise_for(_lib.load().flce_backward_plan(ctypes.byref(problem), int(cu_count), ctypes.byref(rows),
+                                              ctypes.byref(n), ctypes.byref(tile)), "flce_backward_plan")
+    return rows.value, n.value, tile.value
+
+
 def alloc_workspace(problem: _lib.Problem, device) -> torch.Tensor:
     return torch.empty(max(flce_workspace_size(problem), 1), dtype=torch.uint8, device=device)
 

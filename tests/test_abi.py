@@ -282,3 +282,36 @@ def test_chunked_ce_module_arguments():
         L.ChunkedCrossEntropy(reduction="none")
     with pytest.raises(NotImplementedError):
         L.make_ce_problem(4, 10, dtype=__import__("torch").float16)
+
+
+def test_backward_plan_of_the_head_workloads():
+    """The backward's chunk width and dW tile as the planner picks them for 256
+    compute units, as measured best on MI355X (chunk widths in 256-row tiles:
+    96, 250, 144, 114; 384-row dW tiles wherever they measured faster)."""
+    from lm_head_cross_amd import flce_backward_plan
+    cases = {
+        (4096, 4096, 128256, 128256): (96 * 256, 6, 256),
+        (8192, 3072, 262144, 256000): (250 * 256, 4, 384),
+        (16384, 5120, 152064, 152064): (144 * 256, 5, 384),
+        (65536, 8192, 128256, 128256): (114 * 256, 5, 384),
+    }
+    for shape, want in cases.items():
+        assert flce_backward_plan(make_problem(*shape), 256) == want, shape
+
+
+def test_backward_plan_bounds_and_flags():
+    """Every chunk is whole 256-row tiles, at most a quarter of the usable rows
+    (or one tile), the chunks cover Vu, and the dW tile follows the flags."""
+    from lm_head_cross_amd import flce_backward_plan
+    for T, H, V, Vu in ((64, 128, 1000, 1000), (700, 400, 2000, 1900), (4096, 2880, 201088, 200000),
+                        (1000, 512, 3000, 3000), (300, 128, 383, 300), (5, 8, 7, 1)):
+        for cu in (64, 256, 304):
+            rows, n, tile = flce_backward_plan(make_problem(T, H, V, Vu), cu)
+            assert rows % 256 == 0 and rows <= max(256, Vu // 1024 * 256)
+            assert n == -(-Vu // rows) and tile in (256, 384)
+            assert flce_backward_plan(make_problem(T, H, V, Vu, dw_tile=256), cu)[2] == 256
+            if H >= 384:
+                assert flce_backward_plan(make_problem(T, H, V, Vu, dw_tile=384), cu)[2] == 384
+    assert flce_backward_plan(make_problem(0, 128, 1000), 256)[1] == 0
+    with pytest.raises(ValueError):
+        flce_backward_plan(make_problem(64, 128, 1000, 1001), 256)
