@@ -17,11 +17,15 @@ from workloads import make_inputs
 pytestmark = pytest.mark.gpu
 
 
-def _buffers(inp, d):
+def _buffers(inp, d, direct=False, **opts):
+    """Device buffers of one problem; ``direct`` hands an fp32 head to the
+    calls as fp32 (else it is rounded first); ``opts`` go to the problem."""
     X = inp["hidden"].to(d)
     W = inp["weight"].to(d)
     y = inp["labels"].to(d)
-    p = problem_of(inp)
+    if W.dtype == torch.float32 and not direct:
+        W = L.flce_round_to_bf16(W)
+    p = problem_of(inp, W.dtype, **opts)
     T, H, V = p.num_tokens, p.hidden, p.vocab
     out = {
         "loss": torch.empty((), dtype=torch.float32, device=d),
@@ -45,12 +49,23 @@ def _snapshot(o):
     return {k: o[k].clone() for k in ("loss", "lse", "tl", "dX", "dW", "st")}
 
 
-@pytest.mark.parametrize("name", ["multichunk_sum_runs", "ragged_softcap_mean_pad"])
+GRAPH_CASES = {
+    "multichunk_sum_runs": {},
+    "ragged_softcap_mean_pad": {},
+    # the staging pass inside the graph, its copy reused by the backward
+    "fp32_head": dict(direct=True, head_staged=True),
+    # dW on 384-row tiles of Xc^T G
+    "hidden_1152_chunks": dict(dw_tile=384),
+}
+
+
+@pytest.mark.parametrize("name", list(GRAPH_CASES))
 def test_captured_step_replays_match_eager(name):
     d = torch.device("cuda:0")
     inp = make_inputs(SMALL[name])
-    say(f"graph case {name}")
-    p, X, W, y, o = _buffers(inp, d)
+    opts = GRAPH_CASES[name]
+    say(f"graph case {name} {opts}")
+    p, X, W, y, o = _buffers(inp, d, **opts)
     _step(p, X, W, y, o)  # eager (also warms up lazily initialised state)
     torch.cuda.synchronize()
     eager = _snapshot(o)
@@ -63,7 +78,7 @@ def test_captured_step_replays_match_eager(name):
     # a second input set, eager, in buffers of its own
     inp2 = make_inputs(SMALL[name])
     X2 = (inp2["hidden"].float() * 0.5).to(torch.bfloat16).to(d)
-    p2, _, _, _, o2 = _buffers(inp, d)
+    p2, _, _, _, o2 = _buffers(inp, d, **opts)
     _step(p2, X2, W, y, o2)
     torch.cuda.synchronize()
     eager2 = _snapshot(o2)
